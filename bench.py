@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Throughput of the Gemma 3 local/global GQA attention stack on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * prefill leg  : the 27B-shaped block [L,L,L,L,L,G], B=1, S=8192, Hq=32,
+                   Hkv=16, D=128 (QK-RMSNorm + RoPE prologue, flash attention);
+  * decode leg   : 32 sequences with 32768 cached positions, one new token
+                   each, the same six layers (1024-slot rings for local
+                   layers, the full cache for the global one);
+  * chunked leg  : a 4096-query chunk at positions 126976..131071 against a
+                   131072-position cache (global, RoPE base 1e6 with position
+                   interpolation 8) plus the five local layers.
+`value` is the prefill leg's in-window TFLOP/s (4*D flops per visible
+(query head, key) pair over the leg's wall time on the GPU); the decode
+leg's KV GB/s and the chunked leg's TFLOP/s are reported beside it.
+Inputs are seeded synthetic N(0,1) bf16 already resident in HBM.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s (in-window) + decode KV GB/s, 27B shapes, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+LAYERS = 6                  # one 5:1 block
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="prefill,decode,chunked")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle-on-host baseline")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (HBM counter calibration)")
+    return ap.parse_args()
+
+
+class Leg:
+    """Inputs, outputs and workspaces of one leg, all resident in HBM."""
+
+    def __init__(self, name):
+        self.name = name
+        self.calls = []        # callables, one per layer
+        self.work = []         # algorithmic flops or bytes per layer
+        self.unit = ""
+        self.main_ev = []      # (start, stop) events per layer around the main kernel
+
+
+def _events(torch, n):
+    evs = []
+    for _ in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        evs.append((a, b))
+    return evs
+
+
+def build_prefill_leg(torch, G, W, C):
+    w = W.WORKLOADS[2]
+    leg = Leg("prefill")
+    leg.unit = "flop"
+    leg.workload = w
+    leg.inputs = []
+    for l in range(LAYERS):
+        kind = G.layer_kind(l)
+        base = W.ROPE_BASE_GLOBAL if kind == G.GLOBAL else W.ROPE_BASE_LOCAL
+        q = W.device_normal_bf16((w.B, w.S, w.Hq, w.D), W.seed_of(2, l, W.T_Q))
+        k = W.device_normal_bf16((w.B, w.S, w.Hkv, w.D), W.seed_of(2, l, W.T_K))
+        v = W.device_normal_bf16((w.B, w.S, w.Hkv, w.D), W.seed_of(2, l, W.T_V))
+        gq = torch.from_numpy(W.host_gamma(w.D, W.seed_of(2, l, W.T_GQ))).cuda()
+        gk = torch.from_numpy(W.host_gamma(w.D, W.seed_of(2, l, W.T_GK))).cuda()
+        o = torch.empty_like(q)
+        ws = torch.empty(G.prefill_workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device="cuda")
+        leg.inputs.append((q, k, v, gq, gk, kind))
+
+        def call(q=q, k=k, v=v, gq=gq, gk=gk, o=o, ws=ws, kind=kind, base=base):
+            G.prefill(q, k, v, kind, W.WINDOW, base, 1.0, gq, gk, W.EPS, 0.0, None, None, None, o=o, workspace=ws)
+        leg.calls.append(call)
+        leg.work.append(C.prefill_flops(w.B, w.S, w.Hq, w.D, kind == G.LOCAL, W.WINDOW))
+    return leg
+
+
+def build_decode_leg(torch, G, W, C):
+    w = W.WORKLOADS[3]
+    leg = Leg("decode")
+    leg.unit = "byte"
+    leg.workload = w
+    p = w.pos0
+    positions = torch.full((w.B,), p, dtype=torch.int32, device="cuda")
+    for l in range(LAYERS):
+        kind = G.layer_kind(l)
+        base = W.ROPE_BASE_GLOBAL if kind == G.GLOBAL else W.ROPE_BASE_LOCAL
+        cap = W.RING_CAP if kind == G.LOCAL else p + 64  # global: positions 0..p (p+1 slots), padded
+        ck = W.device_normal_bf16((w.B, w.Hkv, cap, w.D), W.seed_of(3, l, W.T_CK))
+        cv = W.device_normal_bf16((w.B, w.Hkv, cap, w.D), W.seed_of(3, l, W.T_CV))
+        cache = G.KVCache(ck, cv, is_ring=(kind == G.LOCAL))
+        q = W.device_normal_bf16((w.B, w.Hq, w.D), W.seed_of(3, l, W.T_Q))
+        kn = W.device_normal_bf16((w.B, w.Hkv, w.D), W.seed_of(3, l, W.T_K))
+        vn = W.device_normal_bf16((w.B, w.Hkv, w.D), W.seed_of(3, l, W.T_V))
+        gq = torch.from_numpy(W.host_gamma(w.D, W.seed_of(3, l, W.T_GQ))).cuda()
+        gk = torch.from_numpy(W.host_gamma(w.D, W.seed_of(3, l, W.T_GK))).cuda()
+        o = torch.empty_like(q)
+        ws = torch.empty(G.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, p, cache), dtype=torch.uint8, device="cuda")
+
+        def call(q=q, kn=kn, vn=vn, cache=cache, gq=gq, gk=gk, o=o, ws=ws, kind=kind, base=base):
+            G.decode(q, kn, vn, positions, p, cache, kind, W.WINDOW, base, 1.0, gq, gk, W.EPS, 0.0, o=o, workspace=ws)
+        leg.calls.append(call)
+        leg.work.append(C.decode_bytes(w.B, w.Hq, w.Hkv, w.D, [p] * w.B, kind == G.LOCAL, W.WINDOW))
+    return leg
+
+
+def build_chunked_leg(torch, G, W, C):
+    w = W.WORKLOADS[4]
+    leg = Leg("chunked")
+    leg.unit = "flop"
+    leg.workload = w
+    p0 = w.pos0
+    for l in range(LAYERS):
+        kind = G.layer_kind(l)
+        if kind == G.GLOBAL:
+            base, scale, cap, ring = W.ROPE_BASE_GLOBAL, w.interp_scale_global, p0 + w.S, False
+        else:
+            base, scale, cap, ring = W.ROPE_BASE_LOCAL, 1.0, W.RING_CAP, True
+        ck = W.device_normal_bf16((w.B, w.Hkv, cap, w.D), W.seed_of(4, l, W.T_CK))
+        cv = W.device_normal_bf16((w.B, w.Hkv, cap, w.D), W.seed_of(4, l, W.T_CV))
+        cache = G.KVCache(ck, cv, is_ring=ring)
+        q = W.device_normal_bf16((w.B, w.S, w.Hq, w.D), W.seed_of(4, l, W.T_Q))
+        k = W.device_normal_bf16((w.B, w.S, w.Hkv, w.D), W.seed_of(4, l, W.T_K))
+        v = W.device_normal_bf16((w.B, w.S, w.Hkv, w.D), W.seed_of(4, l, W.T_V))
+        gq = torch.from_numpy(W.host_gamma(w.D, W.seed_of(4, l, W.T_GQ))).cuda()
+        gk = torch.from_numpy(W.host_gamma(w.D, W.seed_of(4, l, W.T_GK))).cuda()
+        o = torch.empty_like(q)
+        ws = torch.empty(G.prefill_workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device="cuda")
+
+        def call(q=q, k=k, v=v, cache=cache, gq=gq, gk=gk, o=o, ws=ws, kind=kind, base=base, scale=scale):
+            G.prefill(q, k, v, kind, W.WINDOW, base, scale, gq, gk, W.EPS, 0.0, None, [p0], cache, o=o,
+                      workspace=ws)
+        leg.calls.append(call)
+        leg.work.append(C.prefill_flops(w.B, w.S, w.Hq, w.D, kind == G.LOCAL, W.WINDOW, pos0=[p0], has_cache=True,
+                                        ring_capacity=W.RING_CAP if ring else None))
+    return leg
+
+
+def run_leg(torch, G, leg, timed):
+    """Launch the leg's layers; with timing, events bracket the leg and each
+    layer's main kernel (recorded by the library on the launch stream)."""
+    if timed:
+        leg.ev_leg[0].record()
+    for l, call in enumerate(leg.calls):
+        if timed:
+            G.set_timing_events(*leg.main_ev[l])
+        call()
+    if timed:
+        G.set_timing_events(None, None)
+        leg.ev_leg[1].record()
+
+
+def cpu_baseline(torch, W, C, prefill_leg):
+    """The oracle as it stands on the host cores: kv head 0 / query head 0 of
+    each layer of the prefill block, all 8192 query rows."""
+    import numpy as np
+
+    import oracle.attention as A
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = prefill_leg.workload
+    flops = 0.0
+    t_total = 0.0
+    for (q, k, v, gq, gk, kind) in prefill_leg.inputs:
+        qh = q[:, :, 0:1].float().cpu().numpy()
+        kh = k[:, :, 0:1].float().cpu().numpy()
+        vh = v[:, :, 0:1].float().cpu().numpy()
+        base = W.ROPE_BASE_GLOBAL if kind == A.GLOBAL else W.ROPE_BASE_LOCAL
+        t0 = time.perf_counter()
+        A.prefill(qh, kh, vh, kind, W.WINDOW, base, 1.0, gq.cpu().numpy(), gk.cpu().numpy(), W.EPS)
+        t_total += time.perf_counter() - t0
+        flops += C.prefill_flops(1, w.S, 1, w.D, kind == A.LOCAL, W.WINDOW)
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "27B prefill block, query head 0 / kv head 0 of each of the 6 layers, all 8192 rows "
+                      f"(in-window {flops:.4g} flop in {t_total:.2f} s, NumPy float64)"}
+
+
+def _src_hash(name):
+    p = os.path.join(ROOT, "global_gqa_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(kernel_src, launches_key):
+    """Measured HBM bytes per launch from the committed counter summary, if
+    it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        t = json.load(open(p))
+        e = t[launches_key]
+        if e.get("source_sha256_16") != _src_hash(kernel_src):
+            return None
+        return float(e["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is described in the design notes but not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import global_gqa_amd as G
+    import workloads as W
+    from global_gqa_amd import counting as C
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    G.lib()
+    torch.cuda.set_device(0)
+    legs = []
+    names = [s for s in args.legs.split(",") if s]
+    builders = {"prefill": build_prefill_leg, "decode": build_decode_leg, "chunked": build_chunked_leg}
+    for n in names:
+        leg = builders[n](torch, G, W, C)
+        leg.ev_leg = _events(torch, 1)[0]
+        leg.main_ev = _events(torch, LAYERS)
+        legs.append(leg)
+        print(f"[bench] built leg {n}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+
+    for s in range(args.warmup):
+        for leg in legs:
+            run_leg(torch, G, leg, timed=False)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    leg_ms = {leg.name: 0.0 for leg in legs}
+    main_ms = {leg.name: [0.0] * LAYERS for leg in legs}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for leg in legs:
+            run_leg(torch, G, leg, timed=True)
+        torch.cuda.synchronize()
+        for leg in legs:
+            leg_ms[leg.name] += leg.ev_leg[0].elapsed_time(leg.ev_leg[1])
+            for l in range(LAYERS):
+                main_ms[leg.name][l] += leg.main_ev[l][0].elapsed_time(leg.main_ev[l][1])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    K = max(args.steps, 1)
+    print(f"[bench] timed {args.steps} steps in {wall:.2f} s", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    out = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, random-init, in HBM)"}
+    by = {leg.name: leg for leg in legs}
+    if "prefill" in by:
+        leg = by["prefill"]
+        w = leg.workload
+        ms = leg_ms["prefill"] / K
+        flops = sum(leg.work)
+        out["value"] = flops / (ms * 1e-3) / 1e12
+        kms = [x / K for x in main_ms["prefill"]]
+        achieved = flops / (sum(kms) * 1e-3) / 1e12
+        out["config"] = {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                         "layers": "LLLLLG", "window": W.WINDOW, "rope_base": [W.ROPE_BASE_LOCAL, W.ROPE_BASE_GLOBAL],
+                         "in_window_flop_per_block": flops, "prefill_block_ms": ms}
+        out["roofline"] = {"bound": "mfma", "kernel": "prefill_fwd", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                           "traffic": _traffic("prefill.hip", "prefill_fwd_27b_block"),
+                           "launch_ms": kms, "launch_flop": leg.work}
+    if "decode" in by:
+        leg = by["decode"]
+        w = leg.workload
+        ms = leg_ms["decode"] / K
+        nbytes = sum(leg.work)
+        kms = [x / K for x in main_ms["decode"]]
+        # split-K kernel: KV bytes only (q/o/new rows are handled around it)
+        kv_bytes = [b - 2.0 * w.D * (2 * w.B * w.Hq + 2 * w.B * w.Hkv) for b in leg.work]
+        ach = sum(kv_bytes) / (sum(kms) * 1e-3) / 1e9
+        out["decode"] = {"value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "workload": w.name, "ms": ms,
+                         "bytes_per_block": nbytes, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                         "roofline": {"bound": "hbm", "kernel": "decode_splitk", "achieved": ach,
+                                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS,
+                                      "traffic": _traffic("decode.hip", "decode_splitk_27b_block"),
+                                      "launch_ms": kms}}
+    if "chunked" in by:
+        leg = by["chunked"]
+        ms = leg_ms["chunked"] / K
+        flops = sum(leg.work)
+        kms = [x / K for x in main_ms["chunked"]]
+        out["chunked_prefill"] = {"value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                                  "workload": leg.workload.name, "ms": ms, "in_window_flop_per_block": flops,
+                                  "kernel_TFLOPs": flops / (sum(kms) * 1e-3) / 1e12, "launch_ms": kms}
+    if out["value"] is None:
+        out["value"] = 0.0
+    if not args.no_cpu_baseline and "prefill" in by:
+        print("[bench] cpu baseline (oracle on host)...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(torch, W, C, by["prefill"])
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

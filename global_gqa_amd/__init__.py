@@ -1,0 +1,250 @@
+"""Python binding of libg3attn (Gemma 3 local/global GQA attention on MI355X).
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels of ``libg3attn.so``; torch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or fails to load,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+LOCAL = 0
+GLOBAL = 1
+WINDOW = 1024
+RING_CAPACITY = 1024
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libg3attn.so")
+
+G3_OK, G3_EINVAL, G3_EUNSUPPORTED, G3_EHIP, G3_EWORKSPACE = 0, -1, -2, -3, -4
+
+
+class G3Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"g3attn error {code}: {msg}")
+        self.code = code
+
+
+class Span(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("start", ctypes.c_int32), ("end", ctypes.c_int32)]
+
+
+class KVCacheC(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("is_ring", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libg3attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m global_gqa_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    L.g3attn_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32, f32, f32, vp]
+    L.g3attn_qknorm_rope.restype = ctypes.c_int
+    L.g3attn_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp, vp, f32, f32,
+                                 ctypes.POINTER(Span), i32, ctypes.POINTER(i32), ctypes.POINTER(KVCacheC), vp, sz, vp]
+    L.g3attn_prefill.restype = ctypes.c_int
+    L.g3attn_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.g3attn_prefill_workspace_size.restype = sz
+    L.g3attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, ctypes.POINTER(KVCacheC), i32, i32, f32,
+                                f32, vp, vp, f32, f32, vp, sz, vp]
+    L.g3attn_decode.restype = ctypes.c_int
+    L.g3attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(KVCacheC)]
+    L.g3attn_decode_workspace_size.restype = sz
+    L.g3attn_last_error.argtypes = []
+    L.g3attn_last_error.restype = ctypes.c_char_p
+    L.g3attn_version.argtypes = []
+    L.g3attn_version.restype = ctypes.c_int32
+    L.g3attn_set_timing_events.argtypes = [vp, vp]
+    L.g3attn_set_timing_events.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(code: int):
+    if code != G3_OK:
+        raise G3Error(code, lib().g3attn_last_error().decode())
+
+
+def layer_kind(i: int) -> int:
+    """Layer i of the stack is global iff i % 6 == 5: five local layers per
+    global one, the first layer local (Gemma 3 Technical Report, section 2)."""
+    return GLOBAL if i % 6 == 5 else LOCAL
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check_tensor(name, t, dtype, shape=None):
+    import torch
+
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class KVCache:
+    """Per-layer KV cache: k, v device bf16 tensors [B, Hkv, capacity, D]."""
+
+    def __init__(self, k, v, is_ring: bool):
+        import torch
+
+        _check_tensor("cache.k", k, torch.bfloat16)
+        _check_tensor("cache.v", v, torch.bfloat16, k.shape)
+        self.k, self.v, self.is_ring = k, v, bool(is_ring)
+
+    @classmethod
+    def empty(cls, B, Hkv, capacity, D=128, is_ring=False, device="cuda"):
+        import torch
+
+        k = torch.zeros((B, Hkv, capacity, D), dtype=torch.bfloat16, device=device)
+        v = torch.zeros_like(k)
+        return cls(k, v, is_ring)
+
+    @property
+    def capacity(self) -> int:
+        return int(self.k.shape[2])
+
+    def c(self) -> KVCacheC:
+        return KVCacheC(self.k.data_ptr(), self.v.data_ptr(), self.capacity, int(self.is_ring))
+
+
+def qknorm_rope(q, k, positions, q_gamma, k_gamma, eps: float, rope_base: float, interp_scale: float = 1.0,
+                q_out=None, k_out=None, stream=None):
+    """QK-RMSNorm then RoPE of q [T, Hq, D] and/or k [T, Hkv, D] (either may be
+    None).  Returns (q_out, k_out)."""
+    import torch
+
+    ref = q if q is not None else k
+    T, D = ref.shape[0], ref.shape[2]
+    Hq = q.shape[1] if q is not None else 0
+    Hkv = k.shape[1] if k is not None else 0
+    for n, t in (("q", q), ("k", k), ("q_out", q_out), ("k_out", k_out)):
+        _check_tensor(n, t, torch.bfloat16)
+    _check_tensor("positions", positions, torch.int32, (T,))
+    _check_tensor("q_gamma", q_gamma, torch.float32, (D,))
+    _check_tensor("k_gamma", k_gamma, torch.float32, (D,))
+    if q is not None and q_out is None:
+        q_out = torch.empty_like(q)
+    if k is not None and k_out is None:
+        k_out = torch.empty_like(k)
+    _check(lib().g3attn_qknorm_rope(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(q_gamma), _ptr(k_gamma),
+                                    float(eps), _ptr(positions), T, Hq, Hkv, D, float(rope_base),
+                                    float(interp_scale), _stream(stream)))
+    return q_out, k_out
+
+
+def prefill_workspace_size(B, S, Hq, Hkv, D=128) -> int:
+    return int(lib().g3attn_prefill_workspace_size(B, S, Hq, Hkv, D))
+
+
+def decode_workspace_size(B, Hq, Hkv, D, max_position, cache: KVCache) -> int:
+    cc = cache.c()
+    return int(lib().g3attn_decode_workspace_size(B, Hq, Hkv, D, max_position, ctypes.byref(cc)))
+
+
+def _workspace(nbytes, device):
+    import torch
+
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def prefill(q, k, v, layer_kind: int, window: int, rope_base: float, interp_scale: float, q_gamma, k_gamma,
+            eps: float, softmax_scale: float = 0.0, spans: Optional[Sequence[Tuple[int, int, int]]] = None,
+            pos0: Optional[Sequence[int]] = None, cache: Optional[KVCache] = None, o=None, workspace=None,
+            stream=None):
+    """One attention layer's prefill.  q [B, S, Hq, D], k/v [B, S, Hkv, D]
+    raw bf16; spans: (batch, start, end) absolute positions; pos0: first
+    position per sequence; cache: attend to and append into a KV cache."""
+    import torch
+
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _check_tensor("q", q, torch.bfloat16)
+    _check_tensor("k", k, torch.bfloat16, (B, S, Hkv, D))
+    _check_tensor("v", v, torch.bfloat16, (B, S, Hkv, D))
+    _check_tensor("q_gamma", q_gamma, torch.float32, (D,))
+    _check_tensor("k_gamma", k_gamma, torch.float32, (D,))
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("o", o, torch.bfloat16, q.shape)
+    need = prefill_workspace_size(B, S, Hq, Hkv, D)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    sp = None
+    n_sp = 0
+    if spans:
+        n_sp = len(spans)
+        sp = (Span * n_sp)(*[Span(int(b), int(s), int(e)) for (b, s, e) in spans])
+    p0 = None
+    if pos0 is not None:
+        p0 = (ctypes.c_int32 * B)(*[int(x) for x in pos0])
+    cc = ctypes.byref(cache.c()) if cache is not None else None
+    _check(lib().g3attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, S, Hq, Hkv, D, int(layer_kind), int(window),
+                                float(rope_base), float(interp_scale), _ptr(q_gamma), _ptr(k_gamma), float(eps),
+                                float(softmax_scale), sp, n_sp, p0, cc, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
+
+
+def decode(q, k_new, v_new, positions, max_position: int, cache: KVCache, layer_kind: int, window: int,
+           rope_base: float, interp_scale: float, q_gamma, k_gamma, eps: float, softmax_scale: float = 0.0,
+           o=None, workspace=None, stream=None):
+    """One decode step: q [B, Hq, D], k_new/v_new [B, Hkv, D] raw bf16,
+    positions int32 [B] on the device.  Appends to and reads the cache."""
+    import torch
+
+    B, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    _check_tensor("q", q, torch.bfloat16)
+    _check_tensor("k_new", k_new, torch.bfloat16, (B, Hkv, D))
+    _check_tensor("v_new", v_new, torch.bfloat16, (B, Hkv, D))
+    _check_tensor("positions", positions, torch.int32, (B,))
+    _check_tensor("q_gamma", q_gamma, torch.float32, (D,))
+    _check_tensor("k_gamma", k_gamma, torch.float32, (D,))
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("o", o, torch.bfloat16, q.shape)
+    if workspace is None:
+        workspace = _workspace(decode_workspace_size(B, Hq, Hkv, D, max_position, cache), q.device)
+    cc = cache.c()
+    _check(lib().g3attn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(o), B, Hq, Hkv, D, _ptr(positions),
+                               int(max_position), ctypes.byref(cc), int(layer_kind), int(window), float(rope_base),
+                               float(interp_scale), _ptr(q_gamma), _ptr(k_gamma), float(eps), float(softmax_scale),
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
+
+
+def set_timing_events(start_event, stop_event):
+    """Record torch.cuda.Event pair around the next main-kernel launches
+    (None, None to stop).  Events must have been created on the device."""
+    if start_event is None:
+        _check(lib().g3attn_set_timing_events(None, None))
+        return
+    _check(lib().g3attn_set_timing_events(ctypes.c_void_p(start_event.cuda_event),
+                                          ctypes.c_void_p(stop_event.cuda_event)))

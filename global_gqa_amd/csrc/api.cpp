@@ -1,0 +1,348 @@
+// C-ABI layer of libg3attn: argument validation, workspace layout and kernel
+// launches.  Every check runs before the first launch, so a rejected call has
+// no side effects.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/g3attn.h"
+#include "g3_common.hpp"
+#include "g3_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_heads(int32_t Hq, int32_t Hkv, int32_t D) {
+  if (D != g3::kD) return fail(G3_EUNSUPPORTED, "head dim D=%d not supported (only 128)", D);
+  if (Hq <= 0 || Hkv <= 0) return fail(G3_EINVAL, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv) return fail(G3_EINVAL, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(G3_EUNSUPPORTED, "GQA group size Hq/Hkv=%d not supported (1, 2, 4 or 8)", G);
+  return G3_OK;
+}
+
+int check_rope(float rope_base, float interp_scale, float eps) {
+  if (!(rope_base > 1.0f) || !std::isfinite(rope_base)) return fail(G3_EINVAL, "rope_base must be > 1 (got %g)", rope_base);
+  if (!(interp_scale > 0.0f) || !std::isfinite(interp_scale))
+    return fail(G3_EINVAL, "interp_scale must be > 0 (got %g)", interp_scale);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(G3_EINVAL, "eps must be >= 0 (got %g)", eps);
+  return G3_OK;
+}
+
+int check_scale(float softmax_scale, float* sl2) {
+  if (softmax_scale < 0.0f || !std::isfinite(softmax_scale))
+    return fail(G3_EINVAL, "softmax_scale must be >= 0 (0 = D^-1/2), got %g", softmax_scale);
+  const float s = softmax_scale == 0.0f ? 1.0f / std::sqrt((float)g3::kD) : softmax_scale;
+  *sl2 = s * 1.4426950408889634f;
+  return G3_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t prefill_ws(int32_t B, int32_t S, int32_t Hkv, int32_t D) {
+  return round_up((size_t)B * Hkv * S * D * sizeof(uint16_t), 256);
+}
+
+int decode_slots(const g3_kv_cache* c, int32_t max_position) {
+  if (c->is_ring) return c->capacity;
+  const long long n = (long long)max_position + 1;
+  return (int)(n < c->capacity ? n : c->capacity);
+}
+
+int decode_chunks(int n_slots) { return (n_slots + g3::kDecodeChunk - 1) / g3::kDecodeChunk; }
+
+size_t decode_ws(int32_t B, int32_t Hq, int n_chunks) {
+  return round_up((size_t)B * Hq * n_chunks * (g3::kD + 2) * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* g3attn_last_error(void) { return g_err; }
+
+int32_t g3attn_version(void) { return 100; }
+
+int g3attn_set_timing_events(void* start, void* stop) {
+  g_ev_start = (hipEvent_t)start;
+  g_ev_stop = (hipEvent_t)stop;
+  if ((start == nullptr) != (stop == nullptr)) {
+    g_ev_start = g_ev_stop = nullptr;
+    return fail(G3_EINVAL, "timing events must both be set or both be NULL");
+  }
+  return G3_OK;
+}
+
+int g3attn_qknorm_rope(const g3_bf16* q_in, const g3_bf16* k_in, g3_bf16* q_out, g3_bf16* k_out,
+                       const float* q_gamma, const float* k_gamma, float eps, const int32_t* positions,
+                       int32_t T, int32_t Hq, int32_t Hkv, int32_t D, float rope_base, float interp_scale,
+                       void* stream) {
+  g_err[0] = 0;
+  if (D != g3::kD) return fail(G3_EUNSUPPORTED, "head dim D=%d not supported (only 128)", D);
+  if (T < 0) return fail(G3_EINVAL, "T=%d < 0", T);
+  if ((q_in == nullptr) != (q_out == nullptr)) return fail(G3_EINVAL, "q_in and q_out must both be set or NULL");
+  if ((k_in == nullptr) != (k_out == nullptr)) return fail(G3_EINVAL, "k_in and k_out must both be set or NULL");
+  if (q_in && Hq <= 0) return fail(G3_EINVAL, "Hq=%d must be positive", Hq);
+  if (k_in && Hkv <= 0) return fail(G3_EINVAL, "Hkv=%d must be positive", Hkv);
+  if (int e = check_rope(rope_base, interp_scale, eps)) return e;
+  if (T > 0 && positions == nullptr) return fail(G3_EINVAL, "positions is NULL");
+  for (const void* p : {(const void*)q_in, (const void*)k_in, (const void*)q_out, (const void*)k_out})
+    if (p && !aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (T == 0) return G3_OK;
+  hipStream_t st = (hipStream_t)stream;
+  g3::Pos0Table p0t{};
+  p0t.uniform = 1;
+  for (int which = 0; which < 2; ++which) {
+    const g3_bf16* in = which ? k_in : q_in;
+    g3_bf16* out = which ? k_out : q_out;
+    if (!in) continue;
+    g3::RowsArgs a{};
+    a.in = in;
+    a.out = out;
+    a.gamma = which ? k_gamma : q_gamma;
+    a.positions = positions;
+    a.eps = eps;
+    a.T = T;
+    a.H = which ? Hkv : Hq;
+    a.S = T;
+    a.head_major = 0;
+    a.base = rope_base;
+    a.inv_scale = 1.0f / interp_scale;
+    if (hipError_t e = g3::launch_qknorm_rope(a, p0t, st))
+      return fail(G3_EHIP, "qknorm_rope launch failed: %s", hipGetErrorString(e));
+  }
+  return G3_OK;
+}
+
+size_t g3attn_prefill_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D) {
+  (void)Hq;
+  if (B <= 0 || S <= 0 || Hkv <= 0 || D <= 0) return 0;
+  return prefill_ws(B, S, Hkv, D);
+}
+
+int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16* o, int32_t B, int32_t S,
+                   int32_t Hq, int32_t Hkv, int32_t D, int32_t layer_kind, int32_t window, float rope_base,
+                   float interp_scale, const float* q_gamma, const float* k_gamma, float eps, float softmax_scale,
+                   const g3_span* spans, int32_t n_spans, const int32_t* pos0, const g3_kv_cache* cache,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (int e = check_heads(Hq, Hkv, D)) return e;
+  if (B <= 0 || S <= 0) return fail(G3_EINVAL, "B=%d and S=%d must be positive", B, S);
+  if (layer_kind != G3_LOCAL && layer_kind != G3_GLOBAL) return fail(G3_EINVAL, "layer_kind=%d", layer_kind);
+  if (layer_kind == G3_LOCAL && window < 1) return fail(G3_EINVAL, "window=%d < 1", window);
+  if (int e = check_rope(rope_base, interp_scale, eps)) return e;
+  float sl2;
+  if (int e = check_scale(softmax_scale, &sl2)) return e;
+  if (!q || !k || !v || !o) return fail(G3_EINVAL, "q, k, v and o must be non-NULL");
+  for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o})
+    if (!aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
+  if ((long long)B * S * Hq > (1LL << 31) - 1) return fail(G3_EINVAL, "B*S*Hq too large");
+
+  g3::Pos0Table p0t{};
+  p0t.uniform = 1;
+  p0t.v[0] = 0;
+  if (pos0) {
+    bool uni = true;
+    for (int b = 0; b < B; ++b) {
+      if (pos0[b] < 0) return fail(G3_EINVAL, "pos0[%d]=%d < 0", b, pos0[b]);
+      if ((long long)pos0[b] + S > (1LL << 30)) return fail(G3_EINVAL, "pos0[%d]+S out of range", b);
+      if (pos0[b] != pos0[0]) uni = false;
+    }
+    if (!uni && B > g3::kMaxBatchPos0)
+      return fail(G3_EUNSUPPORTED, "per-sequence pos0 supports at most %d sequences", g3::kMaxBatchPos0);
+    p0t.uniform = uni ? 1 : 0;
+    if (uni)
+      p0t.v[0] = pos0[0];
+    else
+      for (int b = 0; b < B; ++b) p0t.v[b] = pos0[b];
+  }
+  auto P0 = [&](int b) { return pos0 ? pos0[b] : 0; };
+
+  g3::SpanTable spt{};
+  if (n_spans < 0 || n_spans > g3::kMaxSpans) return fail(G3_EINVAL, "n_spans=%d (0..%d)", n_spans, g3::kMaxSpans);
+  if (n_spans > 0 && !spans) return fail(G3_EINVAL, "spans is NULL with n_spans=%d", n_spans);
+  spt.n = n_spans;
+  for (int i = 0; i < n_spans; ++i) {
+    const g3_span s = spans[i];
+    if (s.batch < 0 || s.batch >= B) return fail(G3_EINVAL, "span %d: batch %d out of range", i, s.batch);
+    if (s.start >= s.end) return fail(G3_EINVAL, "span %d: empty or reversed [%d, %d)", i, s.start, s.end);
+    if (s.start < P0(s.batch) || s.end > P0(s.batch) + S)
+      return fail(G3_EINVAL, "span %d: [%d, %d) outside the chunk of sequence %d", i, s.start, s.end, s.batch);
+    if (i > 0) {
+      const g3_span p = spans[i - 1];
+      if (p.batch > s.batch || (p.batch == s.batch && p.end > s.start))
+        return fail(G3_EINVAL, "spans must be sorted by (batch, start) and non-overlapping (span %d)", i);
+    }
+    spt.s[i] = g3::Span{s.batch, s.start, s.end};
+  }
+
+  if (cache) {
+    if (!cache->k || !cache->v) return fail(G3_EINVAL, "cache k/v pointers are NULL");
+    if (!aligned16(cache->k) || !aligned16(cache->v)) return fail(G3_EINVAL, "cache pointers must be 16-byte aligned");
+    if (cache->capacity <= 0) return fail(G3_EINVAL, "cache capacity %d", cache->capacity);
+    if (cache->is_ring) {
+      if (layer_kind != G3_LOCAL) return fail(G3_EINVAL, "a ring cache needs a local layer");
+      if (window > cache->capacity) return fail(G3_EINVAL, "window %d exceeds ring capacity %d", window, cache->capacity);
+    } else {
+      for (int b = 0; b < B; ++b)
+        if ((long long)P0(b) + S > cache->capacity)
+          return fail(G3_EINVAL, "linear cache capacity %d < pos0[%d]+S=%lld", cache->capacity, b, (long long)P0(b) + S);
+    }
+  }
+  const size_t need = prefill_ws(B, S, Hkv, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(G3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(G3_EINVAL, "workspace must be 256-byte aligned");
+
+  hipStream_t st = (hipStream_t)stream;
+  uint16_t* khat = (uint16_t*)workspace;
+  {
+    g3::RowsArgs a{};
+    a.in = k;
+    a.out = khat;
+    a.gamma = k_gamma;
+    a.positions = nullptr;
+    a.eps = eps;
+    a.T = B * S;
+    a.H = Hkv;
+    a.S = S;
+    a.head_major = 1;
+    a.base = rope_base;
+    a.inv_scale = 1.0f / interp_scale;
+    if (hipError_t e = g3::launch_qknorm_rope(a, p0t, st))
+      return fail(G3_EHIP, "k prologue launch failed: %s", hipGetErrorString(e));
+  }
+  const int G = Hq / Hkv;
+  g3::PrefillArgs a{};
+  a.q = q;
+  a.khat = khat;
+  a.v = v;
+  a.ck = cache ? cache->k : nullptr;
+  a.cv = cache ? cache->v : nullptr;
+  a.o = o;
+  a.q_gamma = q_gamma;
+  a.eps = eps;
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.cap = cache ? cache->capacity : 0;
+  a.is_ring = cache ? cache->is_ring : 0;
+  a.has_cache = cache ? 1 : 0;
+  a.local = layer_kind == G3_LOCAL;
+  a.window = layer_kind == G3_LOCAL ? window : (1 << 30);
+  a.base = rope_base;
+  a.inv_scale = 1.0f / interp_scale;
+  a.sl2 = sl2;
+  const int rows = g3::prefill_rows_per_wg(G);
+  a.n_qtiles = (S + rows - 1) / rows;
+  if ((long long)B * Hkv * a.n_qtiles > (1LL << 31) - 1) return fail(G3_EINVAL, "grid too large");
+  if (hipError_t e = g3::launch_prefill(a, p0t, spt, G, st, g_ev_start, g_ev_stop))
+    return fail(G3_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
+  if (cache) {
+    g3::AppendArgs ap{};
+    ap.khat = khat;
+    ap.v = v;
+    ap.ck = cache->k;
+    ap.cv = cache->v;
+    ap.B = B;
+    ap.S = S;
+    ap.Hkv = Hkv;
+    ap.cap = cache->capacity;
+    ap.is_ring = cache->is_ring;
+    if (hipError_t e = g3::launch_append_chunk(ap, p0t, st))
+      return fail(G3_EHIP, "cache append launch failed: %s", hipGetErrorString(e));
+  }
+  return G3_OK;
+}
+
+size_t g3attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_position,
+                                    const g3_kv_cache* cache) {
+  (void)Hkv;
+  (void)D;
+  if (!cache || B <= 0 || Hq <= 0 || max_position < 0 || cache->capacity <= 0) return 0;
+  return decode_ws(B, Hq, decode_chunks(decode_slots(cache, max_position)));
+}
+
+int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, g3_bf16* o, int32_t B, int32_t Hq,
+                  int32_t Hkv, int32_t D, const int32_t* positions, int32_t max_position, const g3_kv_cache* cache,
+                  int32_t layer_kind, int32_t window, float rope_base, float interp_scale, const float* q_gamma,
+                  const float* k_gamma, float eps, float softmax_scale, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  g_err[0] = 0;
+  if (int e = check_heads(Hq, Hkv, D)) return e;
+  if (B <= 0) return fail(G3_EINVAL, "B=%d must be positive", B);
+  if (layer_kind != G3_LOCAL && layer_kind != G3_GLOBAL) return fail(G3_EINVAL, "layer_kind=%d", layer_kind);
+  if (layer_kind == G3_LOCAL && window < 1) return fail(G3_EINVAL, "window=%d < 1", window);
+  if (int e = check_rope(rope_base, interp_scale, eps)) return e;
+  float sl2;
+  if (int e = check_scale(softmax_scale, &sl2)) return e;
+  if (!q || !k_new || !v_new || !o || !positions) return fail(G3_EINVAL, "q, k_new, v_new, o, positions must be non-NULL");
+  for (const void* p : {(const void*)q, (const void*)k_new, (const void*)v_new, (const void*)o})
+    if (!aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (!cache || !cache->k || !cache->v) return fail(G3_EINVAL, "decode needs a cache");
+  if (!aligned16(cache->k) || !aligned16(cache->v)) return fail(G3_EINVAL, "cache pointers must be 16-byte aligned");
+  if (cache->capacity <= 0) return fail(G3_EINVAL, "cache capacity %d", cache->capacity);
+  if (max_position < 0) return fail(G3_EINVAL, "max_position %d < 0", max_position);
+  if (cache->is_ring) {
+    if (layer_kind != G3_LOCAL) return fail(G3_EINVAL, "a ring cache needs a local layer");
+    if (window > cache->capacity) return fail(G3_EINVAL, "window %d exceeds ring capacity %d", window, cache->capacity);
+  } else if (max_position >= cache->capacity) {
+    return fail(G3_EINVAL, "max_position %d does not fit a linear cache of capacity %d", max_position, cache->capacity);
+  }
+  const int n_slots = decode_slots(cache, max_position);
+  const int n_chunks = decode_chunks(n_slots);
+  const size_t need = decode_ws(B, Hq, n_chunks);
+  if (!workspace || workspace_bytes < need)
+    return fail(G3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(G3_EINVAL, "workspace must be 256-byte aligned");
+  if ((long long)B * Hkv > 65535) return fail(G3_EUNSUPPORTED, "B*Hkv=%lld exceeds 65535", (long long)B * Hkv);
+
+  g3::DecodeArgs a{};
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.ck = cache->k;
+  a.cv = cache->v;
+  a.positions = positions;
+  a.q_gamma = q_gamma;
+  a.k_gamma = k_gamma;
+  a.ws = (float*)workspace;
+  a.o = o;
+  a.eps = eps;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.cap = cache->capacity;
+  a.is_ring = cache->is_ring;
+  a.local = layer_kind == G3_LOCAL;
+  a.window = layer_kind == G3_LOCAL ? window : (1 << 30);
+  a.max_pos = max_position;
+  a.n_slots = n_slots;
+  a.n_chunks = n_chunks;
+  a.base = rope_base;
+  a.inv_scale = 1.0f / interp_scale;
+  a.sl2 = sl2;
+  if (hipError_t e = g3::launch_decode(a, Hq / Hkv, (hipStream_t)stream, g_ev_start, g_ev_stop))
+    return fail(G3_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+  return G3_OK;
+}
+
+}  // extern "C"

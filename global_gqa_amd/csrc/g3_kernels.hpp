@@ -1,0 +1,80 @@
+// Kernel argument blocks and host launchers shared by the kernels and the
+// C-ABI layer.  Pointers are device pointers; all tensors are bf16 (as
+// uint16_t) unless noted.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "g3_common.hpp"
+
+namespace g3 {
+
+// Rows of QK-RMSNorm + RoPE: T tokens x H heads, input [T][H][D].
+struct RowsArgs {
+  const uint16_t* in;
+  uint16_t* out;          // [T][H][D], or head-major [T/S][H][S][D]
+  const float* gamma;     // fp32 [D] or null (no norm)
+  const int32_t* positions;  // device [T] or null: position = pos0[t / S] + t % S
+  float eps;
+  int T, H, S;            // S: tokens per sequence (for pos0 and head-major)
+  int head_major;
+  float base, inv_scale;
+};
+
+struct AppendArgs {
+  const uint16_t* khat;   // [B][Hkv][S][D]
+  const uint16_t* v;      // [B][S][Hkv][D]
+  uint16_t* ck;           // [B][Hkv][cap][D]
+  uint16_t* cv;
+  int B, S, Hkv, cap, is_ring;
+};
+
+struct PrefillArgs {
+  const uint16_t* q;      // [B][S][Hq][D] raw
+  const uint16_t* khat;   // [B][Hkv][S][D] normed + rotated chunk keys
+  const uint16_t* v;      // [B][S][Hkv][D] raw chunk values
+  const uint16_t* ck;     // cache [B][Hkv][cap][D] (null: no cache)
+  const uint16_t* cv;
+  uint16_t* o;            // [B][S][Hq][D]
+  const float* q_gamma;   // fp32 [D] or null
+  float eps;
+  int B, S, Hq, Hkv;
+  int cap, is_ring, has_cache;
+  int local, window;
+  float base, inv_scale;
+  float sl2;              // softmax_scale * log2(e)
+  int n_qtiles;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;      // [B][Hq][D] raw
+  const uint16_t* k_new;  // [B][Hkv][D] raw
+  const uint16_t* v_new;  // [B][Hkv][D] raw
+  uint16_t* ck;           // [B][Hkv][cap][D]
+  uint16_t* cv;
+  const int32_t* positions;  // device [B]
+  const float* q_gamma;
+  const float* k_gamma;
+  float* ws;              // [B][Hq][n_chunks][D + 2] partials (o, m, l)
+  uint16_t* o;            // [B][Hq][D]
+  float eps;
+  int B, Hq, Hkv, cap, is_ring, local, window;
+  int max_pos;            // clamp bound for positions
+  int n_slots;            // cache slots scanned
+  int n_chunks;
+  float base, inv_scale, sl2;
+};
+
+constexpr int kDecodeChunk = 256;  // cache slots per split-K workgroup
+
+hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, hipStream_t st);
+hipError_t launch_append_chunk(const AppendArgs& a, const Pos0Table& p0t, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt, int G,
+                          hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode(const DecodeArgs& a, int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+
+// Tiles: positions per prefill workgroup for a GQA group of size G.
+inline int prefill_rows_per_wg(int G) { return 4 * (64 / G); }
+
+}  // namespace g3

@@ -1,0 +1,156 @@
+/*
+ * g3attn — Gemma 3 local/global GQA attention stack on AMD Instinct MI355X
+ * (gfx950).  C ABI of the shared library libg3attn.so.
+ *
+ * The stack: five local sliding-window layers (span 1024 tokens, RoPE base
+ * 10k) per global layer (full causal span, RoPE base 1M with linear position
+ * interpolation), grouped-query attention, and QK-RMSNorm in place of logit
+ * soft-capping (Gemma 3 Technical Report, section 1 "Introduction" and
+ * section 2 "Model Architecture").  Image-token spans attend bidirectionally
+ * ("Gemma explained: What's new in Gemma 3", vision section).
+ *
+ * Conventions for every call
+ *   - Tensors are bf16 (uint16_t bit patterns) or fp32, contiguous row-major,
+ *     in DEVICE memory owned by the caller; the head dimension D is innermost.
+ *     Device pointers must be 16-byte aligned.  Arrays documented as host
+ *     memory (spans, pos0) are read during the call only.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  The library allocates nothing, keeps no pointer after it
+ *     returns, holds no mutable global state, and never synchronises.
+ *   - Return value: G3_OK (0) or a negative G3_E* code.  Argument errors are
+ *     detected before any launch and leave every buffer untouched; the text
+ *     of the last error on the calling thread is g3attn_last_error().  A
+ *     device-side fault surfaces at the caller's next synchronisation.
+ *   - GQA: query head h reads KV head h / (Hq / Hkv) (contiguous groups).
+ *   - Supported now: D = 128, Hq / Hkv in {1, 2, 4, 8}.
+ */
+#ifndef G3ATTN_H
+#define G3ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t g3_bf16; /* bfloat16 bit pattern */
+
+enum { G3_LOCAL = 0, G3_GLOBAL = 1 };
+
+enum {
+  G3_OK = 0,
+  G3_EINVAL = -1,       /* bad argument (shape, pointer, alignment, range) */
+  G3_EUNSUPPORTED = -2, /* valid but not implemented (e.g. D != 128) */
+  G3_EHIP = -3,         /* a HIP launch failed */
+  G3_EWORKSPACE = -4    /* workspace missing or too small */
+};
+
+/* One image span: tokens [start, end) of sequence `batch`, in absolute
+ * positions, attend to each other in both directions; text stays causal.
+ * (Gemma explained: bidirectional attention on image inputs.) */
+typedef struct {
+  int32_t batch;
+  int32_t start;
+  int32_t end;
+} g3_span;
+
+/* Per-layer KV cache, caller-owned device memory.
+ * k, v: [B][Hkv][capacity][D] bf16.  K holds keys after QK-RMSNorm and RoPE
+ * at their absolute position; V holds raw values.
+ * is_ring = 0: linear cache, position j lives in slot j (global layers keep
+ *              every position; Technical Report, section 1).
+ * is_ring = 1: ring of the last `capacity` positions, position j in slot
+ *              j mod capacity (local layers only need the last 1024 tokens;
+ *              Technical Report, abstract and section 1).  Requires
+ *              window <= capacity. */
+typedef struct {
+  g3_bf16* k;
+  g3_bf16* v;
+  int32_t capacity;
+  int32_t is_ring;
+} g3_kv_cache;
+
+/* QK-RMSNorm then RoPE, per token and head (Technical Report, section 2:
+ * QK-norm; "Long context": RoPE base, position interpolation; Gemma
+ * explained 27B print: RMSNorm over (128,), eps 1e-6).
+ *   x_hat = x / sqrt(mean(x^2) + eps) * gamma
+ *   pairs (x_k, x_{k+D/2}) rotated by phi = (p / interp_scale) * base^(-2k/D)
+ * q_in/q_out: [T][Hq][D]; k_in/k_out: [T][Hkv][D]; either pair may be NULL
+ * (both members).  In place (q_out == q_in) is allowed.  gamma: device fp32
+ * [D] or NULL for no norm.  positions: device int32 [T], >= 0.
+ * interp_scale > 0 (1 = none). */
+int g3attn_qknorm_rope(const g3_bf16* q_in, const g3_bf16* k_in, g3_bf16* q_out, g3_bf16* k_out,
+                       const float* q_gamma, const float* k_gamma, float eps,
+                       const int32_t* positions, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                       float rope_base, float interp_scale, void* stream);
+
+/* Prefill of one attention layer: prologue (QK-RMSNorm + RoPE) and flash
+ * attention over the visible keys only.
+ * q: [B][S][Hq][D] raw; k, v: [B][S][Hkv][D] raw; o: [B][S][Hq][D].
+ * Token r of sequence b is at position pos0[b] + r (pos0: host int32 [B] or
+ * NULL for all zero).
+ * Visibility of key position j to query position i (same sequence):
+ *   global: j <= i, or i and j in one span;   local: that and |i - j| < window.
+ * layer_kind: G3_LOCAL or G3_GLOBAL (window is ignored for global).
+ * softmax_scale: logit multiplier, 0 means D^-1/2; logits are not capped.
+ * spans: host array of n_spans (<= 64) spans sorted by (batch, start),
+ *   non-overlapping, each inside [pos0[b], pos0[b] + S); NULL if n_spans = 0.
+ * cache: NULL for a self-contained prompt.  Otherwise this is a chunk of a
+ *   longer sequence: positions below pos0[b] are read from the cache (a
+ *   linear cache must hold 0..pos0[b]-1; a ring the last `capacity` of them)
+ *   and, after the attention, the chunk's normed+rotated keys and raw values
+ *   are written to their slots (a ring keeps only its last `capacity`).
+ *   A linear cache needs capacity >= pos0[b] + S.
+ * workspace: device, >= g3attn_prefill_workspace_size(B, S, Hq, Hkv, D)
+ *   bytes, 256-byte aligned; its contents on entry do not matter. */
+int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16* o,
+                   int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                   int32_t layer_kind, int32_t window, float rope_base, float interp_scale,
+                   const float* q_gamma, const float* k_gamma, float eps, float softmax_scale,
+                   const g3_span* spans, int32_t n_spans, const int32_t* pos0,
+                   const g3_kv_cache* cache, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t g3attn_prefill_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D);
+
+/* One decode step: each sequence b adds one token at position positions[b].
+ * q: [B][Hq][D] raw; k_new, v_new: [B][Hkv][D] raw; o: [B][Hq][D].
+ * The new key is normed and rotated, written with v_new to its cache slot,
+ * and the token attends to positions [0, p] (global) or
+ * [max(0, p - window + 1), p] (local), itself included.
+ * positions: device int32 [B]; every entry must lie in [0, max_position]
+ *   (host bound used to size the grid) and, for a linear cache, below
+ *   capacity.  Entries outside that range are clamped by the kernels so no
+ *   access leaves the cache, but the result for that sequence is undefined.
+ * workspace: device, >= g3attn_decode_workspace_size(...) bytes, 256-byte
+ *   aligned; contents on entry do not matter.  Split-K partials are merged in
+ *   a fixed order, so results are bitwise reproducible. */
+int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, g3_bf16* o,
+                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                  const int32_t* positions, int32_t max_position, const g3_kv_cache* cache,
+                  int32_t layer_kind, int32_t window, float rope_base, float interp_scale,
+                  const float* q_gamma, const float* k_gamma, float eps, float softmax_scale,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+size_t g3attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t max_position, const g3_kv_cache* cache);
+
+/* Text of the last error on this thread ("" if none); valid until the next
+ * call on this thread. */
+const char* g3attn_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t g3attn_version(void);
+
+/* Profiling hook for this thread.  When both are non-NULL (hipEvent_t
+ * handles), the next g3attn_prefill / g3attn_decode calls record `start`
+ * immediately before and `stop` immediately after the launch of their main
+ * kernel (the flash-attention kernel of a prefill, the split-K kernel of a
+ * decode), on the call's stream.  Pass NULL, NULL to turn it off. */
+int g3attn_set_timing_events(void* start, void* stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* G3ATTN_H */

@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before any launch (no GPU needed: nothing here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import global_gqa_amd as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "g3attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(g3attn_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(G.LIB_PATH):
+        pytest.skip("libg3attn.so not built")
+    return G.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert {"g3attn_qknorm_rope", "g3attn_prefill", "g3attn_decode"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.g3attn_version() >= 100
+
+
+def test_workspace_sizes(L):
+    assert L.g3attn_prefill_workspace_size(1, 8192, 32, 16, 128) == 16 * 8192 * 128 * 2
+    assert L.g3attn_prefill_workspace_size(0, 8192, 32, 16, 128) == 0
+    ring = G.KVCacheC(0, 0, 1024, 1)
+    lin = G.KVCacheC(0, 0, 40000, 0)
+    # ring: 4 chunks of 256 slots; linear: positions 0..32768 -> 129 chunks
+    assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(ring)) == 32 * 32 * 4 * 130 * 4
+    assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(lin)) == 32 * 32 * 129 * 130 * 4
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address: validation fails before any use
+
+
+def _prefill(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, S=64, Hq=4, Hkv=2, D=128, kind=G.LOCAL, window=1024,
+             base=1e4, scale=1.0, gq=None, gk=None, eps=1e-6, sm=0.0, spans=None, n_spans=0, pos0=None, cache=None,
+             ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.g3attn_prefill(a["q"], a["k"], a["v"], a["o"], a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["kind"],
+                            a["window"], a["base"], a["scale"], a["gq"], a["gk"], a["eps"], a["sm"], a["spans"],
+                            a["n_spans"], a["pos0"], a["cache"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _err(L):
+    return L.g3attn_last_error().decode()
+
+
+def test_prefill_validation_errors(L):
+    assert _prefill(L, D=64) == G.G3_EUNSUPPORTED and "D=64" in _err(L)
+    assert _prefill(L, Hq=6, Hkv=4) == G.G3_EINVAL and "multiple" in _err(L)
+    assert _prefill(L, Hq=6, Hkv=2) == G.G3_EUNSUPPORTED
+    assert _prefill(L, S=0) == G.G3_EINVAL
+    assert _prefill(L, kind=7) == G.G3_EINVAL
+    assert _prefill(L, window=0) == G.G3_EINVAL
+    assert _prefill(L, base=0.5) == G.G3_EINVAL
+    assert _prefill(L, scale=0.0) == G.G3_EINVAL
+    assert _prefill(L, sm=-1.0) == G.G3_EINVAL
+    assert _prefill(L, q=FAKE + 2) == G.G3_EINVAL and "aligned" in _err(L)
+    assert _prefill(L, ws_bytes=10) == G.G3_EWORKSPACE
+    assert _prefill(L, ws=FAKE + 16) == G.G3_EINVAL
+    sp = (G.Span * 2)(G.Span(0, 10, 20), G.Span(0, 15, 30))
+    assert _prefill(L, spans=sp, n_spans=2) == G.G3_EINVAL and "overlapping" in _err(L)
+    sp = (G.Span * 1)(G.Span(0, 60, 70))
+    assert _prefill(L, spans=sp, n_spans=1) == G.G3_EINVAL and "outside" in _err(L)
+    sp = (G.Span * 1)(G.Span(1, 0, 8))
+    assert _prefill(L, spans=sp, n_spans=1) == G.G3_EINVAL
+    assert _prefill(L, n_spans=65, spans=sp) == G.G3_EINVAL
+    ring = G.KVCacheC(FAKE, FAKE, 512, 1)
+    assert _prefill(L, cache=ctypes.byref(ring)) == G.G3_EINVAL and "ring" in _err(L)
+    ring = G.KVCacheC(FAKE, FAKE, 1024, 1)
+    assert _prefill(L, cache=ctypes.byref(ring), kind=G.GLOBAL) == G.G3_EINVAL
+    lin = G.KVCacheC(FAKE, FAKE, 100, 0)
+    p0 = (ctypes.c_int32 * 1)(50)
+    assert _prefill(L, cache=ctypes.byref(lin), pos0=p0) == G.G3_EINVAL and "capacity" in _err(L)
+    p0 = (ctypes.c_int32 * 1)(-1)
+    assert _prefill(L, pos0=p0) == G.G3_EINVAL
+
+
+def test_decode_validation_errors(L):
+    ring = G.KVCacheC(FAKE, FAKE, 1024, 1)
+    lin = G.KVCacheC(FAKE, FAKE, 1000, 0)
+
+    def dec(**kw):
+        a = dict(B=2, Hq=4, Hkv=2, D=128, maxp=500, cache=ctypes.byref(ring), kind=G.LOCAL, window=1024,
+                 ws_bytes=1 << 30, positions=FAKE)
+        a.update(kw)
+        return L.g3attn_decode(FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"], a["D"], a["positions"], a["maxp"],
+                               a["cache"], a["kind"], a["window"], 1e4, 1.0, None, None, 1e-6, 0.0, FAKE,
+                               a["ws_bytes"], None)
+    assert dec(D=256) == G.G3_EUNSUPPORTED
+    assert dec(B=0) == G.G3_EINVAL
+    assert dec(cache=None) == G.G3_EINVAL
+    assert dec(positions=None) == G.G3_EINVAL
+    assert dec(window=2048) == G.G3_EINVAL
+    assert dec(kind=G.GLOBAL) == G.G3_EINVAL
+    assert dec(cache=ctypes.byref(lin), kind=G.GLOBAL, maxp=1000) == G.G3_EINVAL and "capacity" in _err(L)
+    assert dec(ws_bytes=100) == G.G3_EWORKSPACE
+    assert dec(maxp=-1) == G.G3_EINVAL
+
+
+def test_qknorm_rope_validation_errors(L):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, qo=FAKE, ko=FAKE, T=4, Hq=4, Hkv=2, D=128, base=1e4, scale=1.0, pos=FAKE)
+        a.update(kw)
+        return L.g3attn_qknorm_rope(a["q"], a["k"], a["qo"], a["ko"], None, None, 1e-6, a["pos"], a["T"], a["Hq"],
+                                    a["Hkv"], a["D"], a["base"], a["scale"], None)
+    assert call(D=64) == G.G3_EUNSUPPORTED
+    assert call(qo=None) == G.G3_EINVAL
+    assert call(pos=None) == G.G3_EINVAL
+    assert call(scale=-1.0) == G.G3_EINVAL
+    assert call(T=-1) == G.G3_EINVAL
+    assert call(T=0) == G.G3_OK  # nothing to do, nothing launched
+
+
+def test_timing_events_hook_validation(L):
+    assert L.g3attn_set_timing_events(FAKE, None) == G.G3_EINVAL
+    assert L.g3attn_set_timing_events(None, None) == G.G3_OK
+
+
+def test_layer_schedule_matches_oracle():
+    import oracle
+
+    assert [G.layer_kind(i) for i in range(62)] == [oracle.layer_kind(i) for i in range(62)]
