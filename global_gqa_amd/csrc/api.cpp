@@ -56,8 +56,15 @@ int check_scale(float softmax_scale, float* sl2) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-size_t prefill_ws(int32_t B, int32_t S, int32_t Hkv, int32_t D) {
+// Prefill workspace: normed+rotated chunk keys [B][Hkv][S][D] bf16, then one
+// int32 flag per flash workgroup (sized for the smallest tile, G = 1).
+size_t prefill_ws_keys(int32_t B, int32_t S, int32_t Hkv, int32_t D) {
   return round_up((size_t)B * Hkv * S * D * sizeof(uint16_t), 256);
+}
+size_t prefill_ws(int32_t B, int32_t S, int32_t Hkv, int32_t D) {
+  const size_t tiles = (size_t)B * Hkv * ((S + g3::prefill_rows_per_wg(1) - 1) / g3::prefill_rows_per_wg(1)) *
+                       (size_t)8;  // up to 8 query heads per kv head
+  return prefill_ws_keys(B, S, Hkv, D) + round_up(tiles * sizeof(int32_t), 256);
 }
 
 int decode_slots(const g3_kv_cache* c, int32_t max_position) {
@@ -238,6 +245,7 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
   a.cv = cache ? cache->v : nullptr;
   a.o = o;
   a.q_gamma = q_gamma;
+  a.flags = (int*)((char*)workspace + prefill_ws_keys(B, S, Hkv, D));
   a.eps = eps;
   a.B = B;
   a.S = S;

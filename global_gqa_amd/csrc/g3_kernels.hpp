@@ -38,6 +38,7 @@ struct PrefillArgs {
   const uint16_t* cv;
   uint16_t* o;            // [B][S][Hq][D]
   const float* q_gamma;   // fp32 [D] or null
+  int* flags;             // [grid] per-workgroup "redo with the online maximum" flags
   float eps;
   int B, S, Hq, Hkv;
   int cap, is_ring, has_cache;

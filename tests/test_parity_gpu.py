@@ -148,6 +148,31 @@ def test_prefill_mask_probe_exact():
             assert ok, (kind, i, float(got[0, i, 0, 0]), want)
 
 
+@pytest.mark.parametrize("kind", [A.LOCAL, A.GLOBAL])
+def test_prefill_online_max_fallback(kind):
+    """Logits far outside the fast path's exponent range (no QK-norm and
+    inputs scaled by 32 on one sequence; huge gammas on the other call) must
+    take the online-maximum pass and still match the oracle."""
+    B, S, Hq, Hkv = 2, 600, 4, 2
+    q, k, v, gq, gk = _inputs(6, kind, B, S, Hq, Hkv)
+    q = q.copy()
+    k = k.copy()
+    q[1] *= 32.0  # powers of two keep the values exactly representable
+    k[1] *= 32.0
+    base, scale = _kind_params(kind)
+    flat = None
+    o = G.prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), kind, 200, base, scale, None, None, W.EPS, 0.0)
+    torch.cuda.synchronize()
+    ref = A.prefill(q, k, v, kind, 200, base, scale, None, None, W.EPS)
+    assert_parity(host(o)[0], ref[0], "unscaled sequence (fast path)")
+    assert_parity(host(o)[1], ref[1], "scaled sequence (online max)")
+    big = np.full(128, 8.0, dtype=np.float32)
+    got = _run_prefill(q[:1], k[:1], v[:1], big, big, kind, base, scale, window=200)
+    ref = A.prefill(q[:1], k[:1], v[:1], kind, 200, base, scale, big, big, W.EPS)
+    assert_parity(got, ref, "gamma = 8 (online max)")
+    assert flat is None
+
+
 def test_prefill_deterministic():
     q, k, v, gq, gk = _inputs(1, 0, 1, 1000, 4, 2)
     a = _run_prefill(q, k, v, gq, gk, A.GLOBAL, 1e6, 1.0)
