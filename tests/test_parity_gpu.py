@@ -150,27 +150,26 @@ def test_prefill_mask_probe_exact():
 
 @pytest.mark.parametrize("kind", [A.LOCAL, A.GLOBAL])
 def test_prefill_online_max_fallback(kind):
-    """Logits far outside the fast path's exponent range (no QK-norm and
-    inputs scaled by 32 on one sequence; huge gammas on the other call) must
-    take the online-maximum pass and still match the oracle."""
+    """Sequence 1 has logits far outside the fast path's exponent range, so
+    its tiles take the online-maximum pass; sequence 0 stays on the fast path.
+    The inputs keep the logits exact on the GPU (so the comparison is well
+    conditioned even though the softmax is nearly one-hot): no QK-norm,
+    integer-valued q/k, a softmax scale with scale*log2(e) = 4 (a power of
+    two), and an interpolation scale so large that every rotation angle is
+    below 1e-6 rad."""
     B, S, Hq, Hkv = 2, 600, 4, 2
-    q, k, v, gq, gk = _inputs(6, kind, B, S, Hq, Hkv)
-    q = q.copy()
-    k = k.copy()
-    q[1] *= 32.0  # powers of two keep the values exactly representable
-    k[1] *= 32.0
-    base, scale = _kind_params(kind)
-    flat = None
-    o = G.prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), kind, 200, base, scale, None, None, W.EPS, 0.0)
+    rng = np.random.default_rng(21)
+    q = np.round(rng.standard_normal((B, S, Hq, 128))).astype(np.float32)
+    k = np.round(rng.standard_normal((B, S, Hkv, 128))).astype(np.float32)
+    v = W.host_normal_bf16((B, S, Hkv, 128), 22)
+    q[0] *= 1.0 / 64  # dyadic: still exact; keeps sequence 0 on the fast path
+    sm = 4.0 / np.log2(np.e)
+    base = W.ROPE_BASE_LOCAL if kind == A.LOCAL else W.ROPE_BASE_GLOBAL
+    o = G.prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), kind, 200, base, 1e9, None, None, W.EPS, sm)
     torch.cuda.synchronize()
-    ref = A.prefill(q, k, v, kind, 200, base, scale, None, None, W.EPS)
-    assert_parity(host(o)[0], ref[0], "unscaled sequence (fast path)")
-    assert_parity(host(o)[1], ref[1], "scaled sequence (online max)")
-    big = np.full(128, 8.0, dtype=np.float32)
-    got = _run_prefill(q[:1], k[:1], v[:1], big, big, kind, base, scale, window=200)
-    ref = A.prefill(q[:1], k[:1], v[:1], kind, 200, base, scale, big, big, W.EPS)
-    assert_parity(got, ref, "gamma = 8 (online max)")
-    assert flat is None
+    ref = A.prefill(q, k, v, kind, 200, base, 1e9, None, None, W.EPS, sm)
+    assert_parity(host(o)[0], ref[0], "sequence 0 (fast path)")
+    assert_parity(host(o)[1], ref[1], "sequence 1 (online maximum)")
 
 
 def test_prefill_deterministic():
