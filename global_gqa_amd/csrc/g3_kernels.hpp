@@ -76,6 +76,6 @@ hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const Span
 hipError_t launch_decode(const DecodeArgs& a, int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 // Tiles: positions per prefill workgroup for a GQA group of size G.
-inline int prefill_rows_per_wg(int G) { return 4 * (64 / G); }
+inline int prefill_rows_per_wg(int G) { return 4 * (32 / G); }
 
 }  // namespace g3

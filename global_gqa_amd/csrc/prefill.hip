@@ -82,155 +82,99 @@ __device__ __forceinline__ RowRange row_range(int i, int b, int kmin_avail, cons
   return RowRange{lo, hi};
 }
 
-// Per-wave running state of the flash loop.
+// Per-wave running state of the flash loop (one query row per lane).
 struct WaveState {
-  f32x16 o[4][2];   // O^T accumulators [dim block][query block] (stay in AGPRs)
-  float l[2];       // per-lane partial row sums of p
-  float m[2];       // running max (log2 units), online-max mode only
+  f32x16 o[4];   // O^T accumulators [dim block of 32] (stay in AGPRs)
+  float l;       // per-lane partial row sum of p
+  float m;       // running max (log2 units), online-maximum pass only
 };
 
-// S^T block (32 keys x 32 queries per query block) = K[kb] Q^T over D = 128.
-__device__ __forceinline__ void qk_block(const uint16_t* kl, int kb, int ln, int h2, const bf16x8 (&q)[2][8],
-                                         f32x16 (&s)[2]) {
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[qb][r] = 0.f;
-#pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const bf16x8 kop = *(const bf16x8*)(kl + (kb * 32 + ln) * kLdsStride + 16 * st + 8 * h2);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[qb][st], s[qb], 0, 0, 0);
-  }
-}
-
-// p = exp2(s) for one half (scores are pre-scaled into log2 units), masked
-// keys -> 0; returns the B operands (P^T as bf16) of the two 16-key steps.
-// ONLINE: classic running max with rescale of the accumulators.
+// One 64-key tile for one wave of 32 query rows:
+//   S^T (64 keys x 32 queries) = K Q^T      16 MFMA 32x32x16, K from LDS
+//   p = exp2(S) (scores are already in log2 units; masked keys -> 0)
+//   O^T (128 dims x 32 queries) += V^T P^T  16 MFMA, V^T via transposing reads
 template <bool MASK, bool ONLINE>
-__device__ __forceinline__ void softmax_half(f32x16 (&s)[2], int kb, int ts, int h2, const int (&lo)[2],
-                                             const int (&hi)[2], WaveState& w, bf16x8 (&p)[2][2]) {
+__device__ __forceinline__ void tile_body(const uint16_t* kl, const uint16_t* vl, const bf16x8 (&q)[8],
+                                          WaveState& w, int lo, int hi, int ts, int ln, int h2, int tr_off) {
   const float NEG_INF = -__builtin_huge_valf();
+  f32x16 s[2];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    if (MASK) {
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 kop = *(const bf16x8*)(kl + (kb * 32 + ln) * kLdsStride + 16 * st + 8 * h2);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[st], s[kb], 0, 0, 0);
+    }
+  if (MASK) {
+    // key of (kb, r) = ts + 32 kb + 8 (r / 4) + 4 h2 + r % 4
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = ts + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        if (j < lo[qb] || j > hi[qb]) s[qb][r] = NEG_INF;
+        if (j < lo || j > hi) s[kb][r] = NEG_INF;
       }
-    }
-    float off = 0.f;
-    if (ONLINE) {
-      float mx = NEG_INF;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
-      mx = xhalf_max(mx);
-      const float m_new = fmaxf(w.m[qb], mx);
-      off = (m_new == NEG_INF) ? 0.f : m_new;
-      const float alpha = fast_exp2(w.m[qb] - off);
-      w.m[qb] = m_new;
-      w.l[qb] *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) w.o[mb][qb][r] *= alpha;
-    }
-    float rs = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(ONLINE ? s[qb][r] - off : s[qb][r]);
-      s[qb][r] = e;
-      rs += e;
-    }
-    w.l[qb] += rs;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r0 = 8 * t;
-      u32x4 u = {pack2(s[qb][r0], s[qb][r0 + 1]), pack2(s[qb][r0 + 2], s[qb][r0 + 3]),
-                 pack2(s[qb][r0 + 4], s[qb][r0 + 5]), pack2(s[qb][r0 + 6], s[qb][r0 + 7])};
-      p[t][qb] = __builtin_bit_cast(bf16x8, u);
-    }
   }
-}
-
-// O^T += V^T P^T over the 32 keys of half kb (two 16-key steps).
-__device__ __forceinline__ void pv_half(const uint16_t* vl, int kb, int tr_off, const bf16x8 (&p)[2][2],
-                                        WaveState& w) {
+  float off = 0.f;
+  if (ONLINE) {
+    float mx = NEG_INF;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = xhalf_max(mx);
+    const float m_new = fmaxf(w.m, mx);
+    off = (m_new == NEG_INF) ? 0.f : m_new;
+    const float alpha = fast_exp2(w.m - off);
+    w.m = m_new;
+    w.l *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w.o[mb][r] *= alpha;
+  }
+  bf16x8 pb[4];
+  float rs = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = s[t >> 1][8 * (t & 1) + i];
+      e[i] = fast_exp2(ONLINE ? x - off : x);
+      rs += e[i];
+    }
+    u32x4 u = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+    pb[t] = __builtin_bit_cast(bf16x8, u);
+  }
+  w.l += rs;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const uint16_t* base = vl + (32 * kb + 16 * t) * kLdsStride + 32 * mb + tr_off;
+      const uint16_t* base = vl + 16 * t * kLdsStride + 32 * mb + tr_off;
       const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
       const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * kLdsStride));
       const bf16x8 vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        w.o[mb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, p[t][qb], w.o[mb][qb], 0, 0, 0);
+      w.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[t], w.o[mb], 0, 0, 0);
     }
-  }
-}
-
-// One 64-key tile for one wave: QK of both halves, then softmax of half 0
-// (overlapping the MFMAs of half 1), PV of half 0 (overlapping the softmax
-// of half 1), PV of half 1.  Straight-line code, so the scheduler can
-// interleave the independent MFMA and VALU streams.
-template <bool MASK, bool ONLINE>
-__device__ __forceinline__ void tile_body(const uint16_t* kl, const uint16_t* vl, const bf16x8 (&q)[2][8],
-                                          WaveState& w, const int (&lo)[2], const int (&hi)[2], int ts, int ln,
-                                          int h2, int tr_off) {
-  f32x16 s0[2], s1[2];
-  bf16x8 p0[2][2], p1[2][2];
-  qk_block(kl, 0, ln, h2, q, s0);
-  qk_block(kl, 1, ln, h2, q, s1);
-  // scores are consumed by VALU: have the MFMAs write them to VGPRs
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) asm volatile("" : "+v"(s0[qb]), "+v"(s1[qb]));
-  softmax_half<MASK, ONLINE>(s0, 0, ts, h2, lo, hi, w, p0);
-  pv_half(vl, 0, tr_off, p0, w);
-  softmax_half<MASK, ONLINE>(s1, 1, ts, h2, lo, hi, w, p1);
-  pv_half(vl, 1, tr_off, p1, w);
-  if (!ONLINE) {
-    // Issue order: QK of half 0; QK of half 1 interleaved with the softmax
-    // of half 0; PV of half 0 interleaved with the softmax of half 1; PV of
-    // half 1.  (mask bits: 0x8 MFMA, 0x2 VALU, 0x100 LDS read)
-    constexpr int kValuPerMfma = MASK ? 10 : 6;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-  }
 }
 
 }  // namespace
 
+// Workgroup = 4 waves = one (sequence, kv head, query tile).  Each wave owns
+// 32 query rows: 32/G positions x the G query heads that share the kv head,
+// so one K/V tile in LDS serves all G heads.  Two workgroups fit on a CU
+// (<= 256 registers per wave), so every SIMD runs two independent waves and
+// one wave's softmax VALU work overlaps the other's MFMAs.
 template <int G, bool ONLINE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256, 2)
 void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
-  constexpr int P = 64 / G;   // positions per wave
+  constexpr int P = 32 / G;   // positions per wave
   constexpr int WP = 4 * P;   // positions per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kTileElems];
@@ -271,35 +215,21 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   wg_lo = wave_min_i(wg_lo);
   wg_hi = wave_max_i(wg_hi);
 
-  int row_lo[2], row_hi[2], row_pos[2], row_head[2];
-  bool row_ok[2];
-  int w_lo_min = 0x7fffffff, w_hi_max = -0x7fffffff, w_lo_max = -0x7fffffff, w_hi_min = 0x7fffffff;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int r = ln + 32 * qb;
-    const int hg = r / P;
-    const int poff = r - hg * P;
-    const int i = qbase + wave * P + poff;
-    row_pos[qb] = i;
-    row_head[qb] = g * G + hg;
-    row_ok[qb] = i < chunk_end;
-    if (row_ok[qb]) {
-      const RowRange rr = row_range(i, b, kmin_avail, a, spt);
-      row_lo[qb] = rr.lo;
-      row_hi[qb] = rr.hi;
-      w_lo_min = min(w_lo_min, rr.lo);
-      w_hi_max = max(w_hi_max, rr.hi);
-      w_lo_max = max(w_lo_max, rr.lo);
-      w_hi_min = min(w_hi_min, rr.hi);
-    } else {
-      row_lo[qb] = 0x7fffffff;
-      row_hi[qb] = -0x7fffffff;
-    }
+  // this lane's query row: position offset ln % P, head ln / P of the group
+  const int hg = ln / P;
+  const int row_pos = qbase + wave * P + (ln - hg * P);
+  const int row_head = g * G + hg;
+  const bool row_ok = row_pos < chunk_end;
+  int row_lo = 0x7fffffff, row_hi = -0x7fffffff;
+  if (row_ok) {
+    const RowRange rr = row_range(row_pos, b, kmin_avail, a, spt);
+    row_lo = rr.lo;
+    row_hi = rr.hi;
   }
-  w_lo_min = wave_min_i(w_lo_min);
-  w_hi_max = wave_max_i(w_hi_max);
-  w_lo_max = wave_max_i(w_lo_max);
-  w_hi_min = wave_min_i(w_hi_min);
+  const int w_lo_min = wave_min_i(row_ok ? row_lo : 0x7fffffff);
+  const int w_hi_max = wave_max_i(row_ok ? row_hi : -0x7fffffff);
+  const int w_lo_max = wave_max_i(row_ok ? row_lo : -0x7fffffff);
+  const int w_hi_min = wave_min_i(row_ok ? row_hi : 0x7fffffff);
 
   const int t_begin = floor_div64(wg_lo - p0);
   const int t_end = floor_div64(wg_hi - p0);  // inclusive
@@ -310,6 +240,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   const int ld_row = tid >> 4;
   const uint16_t* khat_head = a.khat + ((long long)b * a.Hkv + g) * a.S * kD + ld_col;
   const uint16_t* v_seq = a.v + ((long long)b * a.S * a.Hkv + g) * kD + ld_col;
+  const long long vstride = (long long)a.Hkv * kD;
   const long long cache_off = ((long long)b * a.Hkv + g) * (long long)a.cap * kD + ld_col;
   u32x4 pk[4], pv[4];
   auto load_tile = [&](int t) {
@@ -317,16 +248,17 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = ts + ld_row + 16 * u;
-      const bool in_chunk = j >= p0 && j < chunk_end;
-      const bool in_cache = a.has_cache && j < p0 && j >= kmin_avail;
-      const int r = j - p0;
-      const long long slot = a.is_ring ? (long long)(j % max(a.cap, 1)) : (long long)j;
-      const uint16_t* kp = in_chunk ? khat_head + (long long)r * kD : a.ck + cache_off + slot * kD;
-      const uint16_t* vp = in_chunk ? v_seq + (long long)r * a.Hkv * kD : a.cv + cache_off + slot * kD;
       u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (in_chunk || in_cache) {
-        kk = *(const u32x4*)kp;
-        vv = *(const u32x4*)vp;
+      if (j >= p0) {
+        if (j < chunk_end) {
+          const int r = j - p0;
+          kk = *(const u32x4*)(khat_head + (long long)r * kD);
+          vv = *(const u32x4*)(v_seq + (long long)r * vstride);
+        }
+      } else if (a.has_cache && j >= kmin_avail) {
+        const long long slot = a.is_ring ? (long long)(j % a.cap) : (long long)j;
+        kk = *(const u32x4*)(a.ck + cache_off + slot * kD);
+        vv = *(const u32x4*)(a.cv + cache_off + slot * kD);
       }
       pk[u] = kk;
       pv[u] = vv;
@@ -346,20 +278,20 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   __syncthreads();  // also publishes theta_rev
 
   // ---- Q prologue: load, QK-RMSNorm, RoPE, scale by softmax_scale * log2(e),
-  // round to bf16 (B operand of S^T = K Q^T; scores come out in log2 units)
-  bf16x8 qreg[2][8];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  // round to bf16: the B operand of S^T = K Q^T (lane: query ln, dims
+  // 16 s + 8 h2 + [0, 8)), so scores come out in log2 units.
+  bf16x8 qreg[8];
+  {
     float x[64];
-    if (row_ok[qb]) {
-      const uint16_t* src = a.q + (((long long)b * a.S + (row_pos[qb] - p0)) * a.Hq + row_head[qb]) * kD + 8 * h2;
+    if (row_ok) {
+      const uint16_t* src = a.q + (((long long)b * a.S + (row_pos - p0)) * a.Hq + row_head) * kD + 8 * h2;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const u32x4 w = *(const u32x4*)(src + 16 * s);
+        const u32x4 wv = *(const u32x4*)(src + 16 * s);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[8 * s + 2 * e] = bf_lo(w[e]);
-          x[8 * s + 2 * e + 1] = bf_hi(w[e]);
+          x[8 * s + 2 * e] = bf_lo(wv[e]);
+          x[8 * s + 2 * e + 1] = bf_hi(wv[e]);
         }
       }
     } else {
@@ -383,7 +315,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float sn, cs;
-        rope_sincos(row_pos[qb], theta_rev[16 * s + 8 * h2 + e], sn, cs);
+        rope_sincos(row_pos, theta_rev[16 * s + 8 * h2 + e], sn, cs);
         const float x1 = x[8 * s + e] * rn, x2 = x[8 * (s + 4) + e] * rn;
         x[8 * s + e] = x1 * cs - x2 * sn;
         x[8 * (s + 4) + e] = x1 * sn + x2 * cs;
@@ -391,18 +323,11 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      u32x4 w = {pack2(x[8 * s], x[8 * s + 1]), pack2(x[8 * s + 2], x[8 * s + 3]),
-                 pack2(x[8 * s + 4], x[8 * s + 5]), pack2(x[8 * s + 6], x[8 * s + 7])};
-      qreg[qb][s] = __builtin_bit_cast(bf16x8, w);
+      u32x4 wv = {pack2(x[8 * s], x[8 * s + 1]), pack2(x[8 * s + 2], x[8 * s + 3]),
+                  pack2(x[8 * s + 4], x[8 * s + 5]), pack2(x[8 * s + 6], x[8 * s + 7])};
+      qreg[s] = __builtin_bit_cast(bf16x8, wv);
     }
   }
-
-  // Q is read-only in the tile loop: park it in AGPRs (MFMA reads its B
-  // operand from there directly) so the VGPRs hold scores and loads.
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int s = 0; s < 8; ++s) asm volatile("" : "+a"(qreg[qb][s]));
 
   const int tr_g = lane >> 4;
   const int tr_w = lane & 15;
@@ -414,11 +339,9 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ws.o[mb][qb][r] = 0.f;
-  ws.l[0] = ws.l[1] = 0.f;
-  ws.m[0] = ws.m[1] = -__builtin_huge_valf();
+    for (int r = 0; r < 16; ++r) ws.o[mb][r] = 0.f;
+  ws.l = 0.f;
+  ws.m = -__builtin_huge_valf();
   for (int it = 0; it < n_t; ++it) {
     const int t = t_begin + it;
     const int cur = it & 1;
@@ -431,12 +354,6 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
         tile_body<true, ONLINE>(lds_k[cur], lds_v[cur], qreg, ws, row_lo, row_hi, ts, ln, h2, tr_off);
     }
     if (it + 1 < n_t) store_tile(cur ^ 1);
-    // Keep the O^T accumulators in AGPRs across the loop (they are touched
-    // by MFMA only), leaving the VGPRs to scores, probabilities and loads.
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) asm volatile("" : "+a"(ws.o[mb][qb]));
     __syncthreads();
   }
 
@@ -446,31 +363,24 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   // whose sum leaves [2^-64, 2^64] (possible only for extreme gammas, no
   // norm, or foreign cache contents) raises its flag, and a second launch
   // with ONLINE = true redoes exactly those tiles with the running maximum.
+  const float lt = xhalf_sum(ws.l);
   if (!ONLINE) {
-    bool bad = false;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float lt = xhalf_sum(ws.l[qb]);
-      if (row_ok[qb] && !(lt >= 0x1p-64f && lt <= 0x1p64f)) bad = true;
-    }
+    const bool bad = row_ok && !(lt >= 0x1p-64f && lt <= 0x1p64f);
     const int any_bad = __syncthreads_or(bad);
     if (tid == 0) a.flags[li] = any_bad;
     if (any_bad) return;
   }
 
-  // ---- epilogue: O / l, bf16, store rows [b][pos][head][dims]
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float lt = xhalf_sum(ws.l[qb]);
-    if (!row_ok[qb]) continue;
+  // ---- epilogue: O / l, bf16, store the row [b][pos][head][dims]
+  if (row_ok) {
     const float inv = 1.f / lt;
-    uint16_t* dst = a.o + (((long long)b * a.S + (row_pos[qb] - p0)) * a.Hq + row_head[qb]) * kD;
+    uint16_t* dst = a.o + (((long long)b * a.S + (row_pos - p0)) * a.Hq + row_head) * kD;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * mb + 8 * q4 + 4 * h2;
-        const f32x16& oa = ws.o[mb][qb];
+        const f32x16& oa = ws.o[mb];
         *(u32x2*)(dst + d) = u32x2{pack2(oa[4 * q4] * inv, oa[4 * q4 + 1] * inv),
                                    pack2(oa[4 * q4 + 2] * inv, oa[4 * q4 + 3] * inv)};
       }
