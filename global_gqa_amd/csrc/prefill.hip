@@ -37,8 +37,14 @@ namespace g3 {
 namespace {
 
 constexpr int kBN = 64;           // keys per LDS tile (two halves of 32)
-constexpr int kLdsStride = 144;   // bf16 elements per LDS row: 256 B + 32 B pad (conflict-free reads)
-constexpr int kTileElems = kBN * kLdsStride;
+// LDS row strides (bf16 elements).  K rows are read 16 B per lane by 32
+// lanes of different rows (S^T A operand): 256 + 16 B spreads 8 consecutive
+// rows over all 32 banks.  V rows are read by ds_read_b64_tr_b16 in groups of
+// 16 lanes covering 4 rows x 32 B: 256 + 32 B puts those rows on disjoint banks.
+constexpr int kLdsStrideK = 136;
+constexpr int kLdsStrideV = 144;
+constexpr int kTileElemsK = kBN * kLdsStrideK;
+constexpr int kTileElemsV = kBN * kLdsStrideV;
 
 __device__ __forceinline__ int wave_min_i(int x) {
 #pragma unroll
@@ -106,7 +112,7 @@ __device__ __forceinline__ void tile_body(const uint16_t* kl, const uint16_t* vl
   for (int st = 0; st < 8; ++st)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 kop = *(const bf16x8*)(kl + (kb * 32 + ln) * kLdsStride + 16 * st + 8 * h2);
+      const bf16x8 kop = *(const bf16x8*)(kl + (kb * 32 + ln) * kLdsStrideK + 16 * st + 8 * h2);
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[st], s[kb], 0, 0, 0);
     }
   if (MASK) {
@@ -156,9 +162,9 @@ __device__ __forceinline__ void tile_body(const uint16_t* kl, const uint16_t* vl
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const uint16_t* base = vl + 16 * t * kLdsStride + 32 * mb + tr_off;
+      const uint16_t* base = vl + 16 * t * kLdsStrideV + 32 * mb + tr_off;
       const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
-      const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * kLdsStride));
+      const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * kLdsStrideV));
       const bf16x8 vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       w.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[t], w.o[mb], 0, 0, 0);
     }
@@ -176,8 +182,8 @@ __global__ __launch_bounds__(256, 2)
 void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   constexpr int P = 32 / G;   // positions per wave
   constexpr int WP = 4 * P;   // positions per workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kTileElemsK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kTileElemsV];
   __shared__ double theta_rev[64];
 
   const int tid = threadIdx.x;
@@ -243,33 +249,37 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   const long long vstride = (long long)a.Hkv * kD;
   const long long cache_off = ((long long)b * a.Hkv + g) * (long long)a.cap * kD + ld_col;
   u32x4 pk[4], pv[4];
+  // Branch-free: every lane always loads from a valid address (row 0 of this
+  // head's chunk when its key does not exist) and zeroes the data after, so
+  // all eight 16-byte loads of a tile are in flight together.
+  bool pvalid[4];
   auto load_tile = [&](int t) {
     const int ts = p0 + t * kBN;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = ts + ld_row + 16 * u;
-      u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (j >= p0) {
-        if (j < chunk_end) {
-          const int r = j - p0;
-          kk = *(const u32x4*)(khat_head + (long long)r * kD);
-          vv = *(const u32x4*)(v_seq + (long long)r * vstride);
-        }
-      } else if (a.has_cache && j >= kmin_avail) {
+      const bool in_chunk = j >= p0 && j < chunk_end;
+      const bool in_cache = a.has_cache && j < p0 && j >= kmin_avail;
+      const int r = in_chunk ? j - p0 : 0;
+      const uint16_t* kp = khat_head + (long long)r * kD;
+      const uint16_t* vp = v_seq + (long long)r * vstride;
+      if (in_cache) {
         const long long slot = a.is_ring ? (long long)(j % a.cap) : (long long)j;
-        kk = *(const u32x4*)(a.ck + cache_off + slot * kD);
-        vv = *(const u32x4*)(a.cv + cache_off + slot * kD);
+        kp = a.ck + cache_off + slot * kD;
+        vp = a.cv + cache_off + slot * kD;
       }
-      pk[u] = kk;
-      pv[u] = vv;
+      pk[u] = *(const u32x4*)kp;
+      pv[u] = *(const u32x4*)vp;
+      pvalid[u] = in_chunk || in_cache;
     }
   };
   auto store_tile = [&](int buf) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int row = ld_row + 16 * u;
-      *(u32x4*)(&lds_k[buf][row * kLdsStride + ld_col]) = pk[u];
-      *(u32x4*)(&lds_v[buf][row * kLdsStride + ld_col]) = pv[u];
+      *(u32x4*)(&lds_k[buf][row * kLdsStrideK + ld_col]) = pvalid[u] ? pk[u] : zero;
+      *(u32x4*)(&lds_v[buf][row * kLdsStrideV + ld_col]) = pvalid[u] ? pv[u] : zero;
     }
   };
 
@@ -333,7 +343,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   const int tr_w = lane & 15;
   // transposing-read offset (ds_read_b64_tr_b16 works on groups of 16 lanes):
   // key row 4*(group/2) + w/4 (+ 16 t + 8 r), dims 16*(group&1) + 4*(w&3) (+ 32 mb)
-  const int tr_off = (4 * (tr_g >> 1) + (tr_w >> 2)) * kLdsStride + 16 * (tr_g & 1) + 4 * (tr_w & 3);
+  const int tr_off = (4 * (tr_g >> 1) + (tr_w >> 2)) * kLdsStrideV + 16 * (tr_g & 1) + 4 * (tr_w & 3);
 
   WaveState ws;
 #pragma unroll
