@@ -73,7 +73,19 @@ int decode_slots(const g3_kv_cache* c, int32_t max_position) {
   return (int)(n < c->capacity ? n : c->capacity);
 }
 
-int decode_chunks(int n_slots) { return (n_slots + g3::kDecodeChunk - 1) / g3::kDecodeChunk; }
+// Split-K shape: splits of 256 * k slots with k chosen so the grid has about
+// 4096 workgroups (16 per CU) and each keeps its loads streaming long enough.
+int decode_split(int n_slots, int32_t B, int32_t Hkv) {
+  const long long units = (long long)((n_slots + g3::kDecodeChunk - 1) / g3::kDecodeChunk) * B * Hkv;
+  long long k = units / 4096;
+  if (k < 1) k = 1;
+  if (k > 16) k = 16;
+  return (int)k * g3::kDecodeChunk;
+}
+int decode_chunks(int n_slots, int32_t B, int32_t Hkv) {
+  const int split = decode_split(n_slots, B, Hkv);
+  return (n_slots + split - 1) / split;
+}
 
 size_t decode_ws(int32_t B, int32_t Hq, int n_chunks) {
   return round_up((size_t)B * Hq * n_chunks * (g3::kD + 2) * sizeof(float), 256);
@@ -283,10 +295,9 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
 
 size_t g3attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_position,
                                     const g3_kv_cache* cache) {
-  (void)Hkv;
   (void)D;
-  if (!cache || B <= 0 || Hq <= 0 || max_position < 0 || cache->capacity <= 0) return 0;
-  return decode_ws(B, Hq, decode_chunks(decode_slots(cache, max_position)));
+  if (!cache || B <= 0 || Hq <= 0 || Hkv <= 0 || max_position < 0 || cache->capacity <= 0) return 0;
+  return decode_ws(B, Hq, decode_chunks(decode_slots(cache, max_position), B, Hkv));
 }
 
 int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, g3_bf16* o, int32_t B, int32_t Hq,
@@ -316,7 +327,8 @@ int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, 
     return fail(G3_EINVAL, "max_position %d does not fit a linear cache of capacity %d", max_position, cache->capacity);
   }
   const int n_slots = decode_slots(cache, max_position);
-  const int n_chunks = decode_chunks(n_slots);
+  const int split = decode_split(n_slots, B, Hkv);
+  const int n_chunks = decode_chunks(n_slots, B, Hkv);
   const size_t need = decode_ws(B, Hq, n_chunks);
   if (!workspace || workspace_bytes < need)
     return fail(G3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
@@ -344,6 +356,7 @@ int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, 
   a.window = layer_kind == G3_LOCAL ? window : (1 << 30);
   a.max_pos = max_position;
   a.n_slots = n_slots;
+  a.split = split;
   a.n_chunks = n_chunks;
   a.base = rope_base;
   a.inv_scale = 1.0f / interp_scale;

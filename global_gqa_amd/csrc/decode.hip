@@ -8,21 +8,19 @@
 // [0, p] (global) or (p - window, p] (local).  GQA: the G query heads of a kv
 // group share every K/V byte read (Technical Report, section 2).
 //
-// Pure HBM streaming: each workgroup owns (sequence, kv head, chunk of 256
-// cache slots), loads the chunk's K and V rows once with 16-byte coalesced
-// loads (all issued up front), scores every slot for all G heads (two-pass:
-// exact chunk max, then exp and PV, so no rescaling), and writes an
-// unnormalised partial (o, m, l).  A second kernel merges the partials of a
-// head in fixed chunk order, so results are bitwise reproducible.
+// Pure HBM streaming: each workgroup owns (sequence, kv head, split of the
+// cache slots) and streams the split's K and V rows once with 16-byte
+// coalesced non-temporal loads, each wave keeping eight steps of loads in
+// flight.  Sixteen lanes share a key row (8 dims each, DPP row reductions)
+// and all G heads of the group use every row.  The partial (o, m, l) of the
+// split goes to the workspace; a second kernel merges the partials of a head
+// in ascending split order, so results are bitwise reproducible.
 #include "g3_common.hpp"
 #include "g3_kernels.hpp"
 
 namespace g3 {
 
 namespace {
-constexpr int kL = kDecodeChunk;       // slots per workgroup
-constexpr int kKeysPerWave = kL / 4;    // 64
-constexpr int kSteps = kKeysPerWave / 4;  // 16 steps of 4 keys per wave
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -58,14 +56,121 @@ __device__ __forceinline__ float round_bf16(float x) {
 }
 }  // namespace
 
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), result in all 16.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad xor 1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // quad xor 2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // half mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // row mirror
+  return x;
+}
+
+// Per-lane running state of one kv group's G heads over the keys this lane's
+// 16-lane group sees (dims 8*j16 .. 8*j16+7 of the accumulator).
+template <int G>
+struct StreamState {
+  float m[G], l[G], acc[G][8];
+  int nvis;  // visible keys seen by this lane
+};
+
+// Stream the split's slots: step st covers 16 consecutive slots (4 per wave,
+// one per 16-lane group); each step's K and V rows are loaded kDepth steps
+// ahead so the memory pipe never drains.  ONLINE = false: p = exp2(s)
+// directly (QK-RMSNorm bounds the logits); ONLINE = true: running maximum.
+template <int G, bool ONLINE>
+__device__ __forceinline__ void stream_split(const DecodeArgs& a, const float (&qv)[G][8], const float* kn,
+                                             const float* vn, long long head_base, int s0, int nsteps, int p,
+                                             int p_mod, int s_new, int wave, int lane, StreamState<G>& st) {
+  constexpr int kDepth = 8;
+  const int j16 = lane & 15;
+  const int kg = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = ONLINE ? -__builtin_huge_valf() : 0.f;
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
+  }
+  st.nvis = 0;
+  u32x4 kb[kDepth], vb[kDepth];
+  auto slot_of = [&](int step) { return s0 + 16 * step + 4 * wave + kg; };
+  auto issue = [&](int step, int d) {
+    int slot = slot_of(step);
+    if (slot >= a.n_slots) slot = 0;  // stays in bounds; masked below
+    const long long off = (head_base + slot) * kD + 8 * j16;
+    kb[d] = __builtin_nontemporal_load((const u32x4*)(a.ck + off));
+    vb[d] = __builtin_nontemporal_load((const u32x4*)(a.cv + off));
+  };
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (d < nsteps) issue(d, d);
+  for (int st0 = 0; st0 < nsteps; st0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int step = st0 + d;
+      if (step < nsteps) {
+        const int slot = slot_of(step);
+        bool vis = slot < a.n_slots;
+        if (a.is_ring) {
+          int dist = p_mod - slot;
+          if (dist < 0) dist += a.cap;
+          vis = vis && (p - dist >= 0) && (!a.local || dist < a.window);
+        } else {
+          vis = vis && slot <= p && (!a.local || p - slot < a.window);
+        }
+        float kf[8], vf[8];
+        if (slot == s_new) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kf[e] = kn[8 * j16 + e];
+            vf[e] = vn[8 * j16 + e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kf[2 * e] = bf_lo(kb[d][e]);
+            kf[2 * e + 1] = bf_hi(kb[d][e]);
+            vf[2 * e] = bf_lo(vb[d][e]);
+            vf[2 * e + 1] = bf_hi(vb[d][e]);
+          }
+        }
+        if (step + kDepth < nsteps) issue(step + kDepth, d);
+        st.nvis += vis ? 1 : 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float dot = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dot += qv[h][e] * kf[e];
+          const float sc = row16_sum(dot);
+          float pr;
+          if (ONLINE) {
+            const float m_new = vis ? fmaxf(st.m[h], sc) : st.m[h];
+            const float alpha = (m_new == st.m[h]) ? 1.f : fast_exp2(st.m[h] - m_new);
+            pr = vis ? fast_exp2(sc - m_new) : 0.f;
+            st.m[h] = m_new;
+            st.l[h] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.acc[h][e] *= alpha;
+          } else {
+            pr = vis ? fast_exp2(sc) : 0.f;
+          }
+          st.l[h] += pr;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st.acc[h][e] += pr * vf[e];
+        }
+      }
+    }
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void decode_splitk(DecodeArgs a) {
-  __shared__ float qh[G][kD];
   __shared__ float kn[kD];
   __shared__ float vn[kD];
-  __shared__ float sc[G][kL];
-  __shared__ float red[4][G][kD];
-  __shared__ float stat[G][2];
+  __shared__ float part_m[4][4][G];            // [wave][key group][head]
+  __shared__ float part_l[4][4][G];
+  __shared__ float part_acc[4][4][G][kD];      // unnormalised, relative to part_m
+  __shared__ int bad_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x;
@@ -73,18 +178,21 @@ __global__ __launch_bounds__(256) void decode_splitk(DecodeArgs a) {
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   int p = a.positions[b];
   p = max(0, min(p, a.max_pos));
-  const int s0 = c * kL;
+  const int s0 = c * a.split;
+  const int s_end = min(s0 + a.split, a.n_slots);
+  const int nsteps = (s_end - s0 + 15) / 16;
   const int s_new = a.is_ring ? (p % a.cap) : p;
-  const bool owner = s_new >= s0 && s_new < s0 + kL;
+  const int p_mod = a.is_ring ? (p % a.cap) : p;
+  const bool owner = s_new >= s0 && s_new < s_end;
   const long long head_base = ((long long)b * a.Hkv + g) * (long long)a.cap;
   float* part = a.ws + (((long long)b * a.Hq + g * G) * a.n_chunks + c) * (kD + 2);
   const long long head_stride = (long long)a.n_chunks * (kD + 2);
 
-  // Whole chunk invisible (linear cache past p, or before the window)?
+  // Whole split invisible (linear cache past p, or before the window)?
   bool empty = false;
   if (!a.is_ring) {
     if (s0 > p) empty = true;
-    if (a.local && s0 + kL - 1 < p - a.window + 1) empty = true;
+    if (a.local && s_end - 1 < p - a.window + 1) empty = true;
   }
   if (empty) {
     for (int x = tid; x < G * (kD + 2); x += 256) {
@@ -94,170 +202,94 @@ __global__ __launch_bounds__(256) void decode_splitk(DecodeArgs a) {
     return;
   }
 
-  // ---- issue all K and V loads of this wave's 64 slots (16 B per lane per slot)
-  const int j16 = lane & 15;   // dims [8 j16, 8 j16 + 8)
-  const int kg = lane >> 4;    // key within a step of 4
-  u32x4 kr[kSteps], vr[kSteps];
-#pragma unroll
-  for (int st = 0; st < kSteps; ++st) {
-    const int slot = s0 + wave * kKeysPerWave + 4 * st + kg;
-    u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (slot < a.n_slots && slot != s_new) {
-      const long long off = (head_base + slot) * kD + 8 * j16;
-      kk = __builtin_nontemporal_load((const u32x4*)(a.ck + off));
-      vv = __builtin_nontemporal_load((const u32x4*)(a.cv + off));
-    }
-    kr[st] = kk;
-    vr[st] = vv;
-  }
-
-  // ---- q_hat for the G heads (and k_hat/v of the new token in its owner)
-  for (int hg = wave; hg < G; hg += 4) {
-    float y0, y1;
-    norm_rope_vec(a.q + ((long long)b * a.Hq + g * G + hg) * kD, a.q_gamma, a.eps, p, a.base, a.inv_scale,
-                  lane, y0, y1);
-    qh[hg][lane] = round_bf16(y0);
-    qh[hg][lane + 64] = round_bf16(y1);
-  }
-  if (owner && wave == 3) {
-    float y0, y1;
-    const long long src = ((long long)b * a.Hkv + g) * kD;
-    norm_rope_vec(a.k_new + src, a.k_gamma, a.eps, p, a.base, a.inv_scale, lane, y0, y1);
-    const uint32_t w = pack2(y0, y1);
-    kn[lane] = bf_lo(w);
-    kn[lane + 64] = bf_hi(w);
-    const uint16_t v0 = a.v_new[src + lane], v1 = a.v_new[src + lane + 64];
-    vn[lane] = __uint_as_float((uint32_t)v0 << 16);
-    vn[lane + 64] = __uint_as_float((uint32_t)v1 << 16);
-    a.ck[(head_base + s_new) * kD + lane] = (uint16_t)(w & 0xffffu);
-    a.ck[(head_base + s_new) * kD + lane + 64] = (uint16_t)(w >> 16);
-    a.cv[(head_base + s_new) * kD + lane] = v0;
-    a.cv[(head_base + s_new) * kD + lane + 64] = v1;
-  }
-  __syncthreads();
-
-  // ---- pass 1: scores for every slot and head
+  // q_hat for the G heads, scaled by softmax_scale * log2(e) (scores in log2
+  // units), and k_hat / v of the new token in the workgroup that owns its slot
+  const int j16 = lane & 15;
   float qv[G][8];
-#pragma unroll
-  for (int hg = 0; hg < G; ++hg)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[hg][e] = qh[hg][8 * j16 + e];
-  const float NEG_INF = -__builtin_huge_valf();
-#pragma unroll
-  for (int st = 0; st < kSteps; ++st) {
-    const int slot = s0 + wave * kKeysPerWave + 4 * st + kg;
-    float kf[8];
-    if (slot == s_new) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[e] = kn[8 * j16 + e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = bf_lo(kr[st][e]);
-        kf[2 * e + 1] = bf_hi(kr[st][e]);
-      }
+  {
+    __shared__ float qh[G][kD];
+    for (int hg = wave; hg < G; hg += 4) {
+      float y0, y1;
+      norm_rope_vec(a.q + ((long long)b * a.Hq + g * G + hg) * kD, a.q_gamma, a.eps, p, a.base, a.inv_scale,
+                    lane, y0, y1);
+      qh[hg][lane] = round_bf16(y0 * a.sl2);
+      qh[hg][lane + 64] = round_bf16(y1 * a.sl2);
     }
-    // visibility of this slot
-    bool vis = slot < a.n_slots;
-    if (vis) {
-      if (a.is_ring) {
-        const int d = ((p - slot) % a.cap + a.cap) % a.cap;
-        const int jpos = p - d;
-        vis = jpos >= 0 && (!a.local || d < a.window);
-      } else {
-        vis = slot <= p && (!a.local || p - slot < a.window);
-      }
+    if (owner && wave == 3) {
+      float y0, y1;
+      const long long src = ((long long)b * a.Hkv + g) * kD;
+      norm_rope_vec(a.k_new + src, a.k_gamma, a.eps, p, a.base, a.inv_scale, lane, y0, y1);
+      const uint32_t w = pack2(y0, y1);
+      kn[lane] = bf_lo(w);
+      kn[lane + 64] = bf_hi(w);
+      const uint16_t v0 = a.v_new[src + lane], v1 = a.v_new[src + lane + 64];
+      vn[lane] = __uint_as_float((uint32_t)v0 << 16);
+      vn[lane + 64] = __uint_as_float((uint32_t)v1 << 16);
+      a.ck[(head_base + s_new) * kD + lane] = (uint16_t)(w & 0xffffu);
+      a.ck[(head_base + s_new) * kD + lane + 64] = (uint16_t)(w >> 16);
+      a.cv[(head_base + s_new) * kD + lane] = v0;
+      a.cv[(head_base + s_new) * kD + lane + 64] = v1;
     }
-#pragma unroll
-    for (int hg = 0; hg < G; ++hg) {
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) d += qv[hg][e] * kf[e];
-      d += __shfl_xor(d, 8, 16);
-      d += __shfl_xor(d, 4, 16);
-      d += __shfl_xor(d, 2, 16);
-      d += __shfl_xor(d, 1, 16);
-      if (j16 == 0) sc[hg][wave * kKeysPerWave + 4 * st + kg] = vis ? d : NEG_INF;
-    }
-  }
-  __syncthreads();
-
-  // ---- chunk max, probabilities and their sum (wave hg handles head hg)
-  for (int hg = wave; hg < G; hg += 4) {
-    float m = NEG_INF;
-    for (int x = lane; x < kL; x += 64) m = fmaxf(m, sc[hg][x]);
-    m = wave_max(m);
-    const float mu = (m == NEG_INF) ? 0.f : m;
-    float l = 0.f;
-    for (int x = lane; x < kL; x += 64) {
-      const float pr = fast_exp2((sc[hg][x] - mu) * a.sl2);
-      sc[hg][x] = pr;
-      l += pr;
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      stat[hg][0] = m;
-      stat[hg][1] = l;
-    }
-  }
-  __syncthreads();
-
-  // ---- pass 2: acc[hg][dims] = sum_slots p * v
-  float acc[G][8];
-#pragma unroll
-  for (int hg = 0; hg < G; ++hg)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hg][e] = 0.f;
-#pragma unroll
-  for (int st = 0; st < kSteps; ++st) {
-    const int sl = wave * kKeysPerWave + 4 * st + kg;
-    float vf[8];
-    if (s0 + sl == s_new) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vf[e] = vn[8 * j16 + e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[2 * e] = bf_lo(vr[st][e]);
-        vf[2 * e + 1] = bf_hi(vr[st][e]);
-      }
-    }
-#pragma unroll
-    for (int hg = 0; hg < G; ++hg) {
-      const float pr = sc[hg][sl];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hg][e] += pr * vf[e];
-    }
-  }
-  // reduce over the 4 key groups of the wave (lanes j16 + 16 kg)
-#pragma unroll
-  for (int hg = 0; hg < G; ++hg)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = acc[hg][e];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      acc[hg][e] = x;
-    }
-  if (kg == 0) {
+    if (tid == 0) bad_flag = 0;
+    __syncthreads();
 #pragma unroll
     for (int hg = 0; hg < G; ++hg)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[wave][hg][8 * j16 + e] = acc[hg][e];
+      for (int e = 0; e < 8; ++e) qv[hg][e] = qh[hg][8 * j16 + e];
   }
+
+  StreamState<G> st;
+  stream_split<G, false>(a, qv, kn, vn, head_base, s0, nsteps, p, p_mod, s_new, wave, lane, st);
+  // The fast pass needs no running maximum because QK-RMSNorm bounds the
+  // logits; if a sum leaves [2^-64, 2^64] (extreme gammas, no norm, foreign
+  // cache contents) the split is streamed again with the running maximum.
+  bool bad = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) bad = bad || !(st.l[h] <= 0x1p64f) || (st.nvis > 0 && !(st.l[h] >= 0x1p-64f));
+  if (bad) bad_flag = 1;
   __syncthreads();
-  for (int x = tid; x < G * kD; x += 256) {
-    const int hg = x / kD, d = x - hg * kD;
-    part[hg * head_stride + d] = red[0][hg][d] + red[1][hg][d] + red[2][hg][d] + red[3][hg][d];
+  if (bad_flag) stream_split<G, true>(a, qv, kn, vn, head_base, s0, nsteps, p, p_mod, s_new, wave, lane, st);
+
+  // ---- merge the 16 partial states (4 waves x 4 key groups) of each head
+  if (j16 == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      part_m[wave][lane >> 4][h] = st.m[h];
+      part_l[wave][lane >> 4][h] = st.l[h];
+    }
   }
-  if (tid < G) {
-    part[tid * head_stride + kD] = stat[tid][0];
-    part[tid * head_stride + kD + 1] = stat[tid][1];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part_acc[wave][lane >> 4][h][8 * j16 + e] = st.acc[h][e];
+  __syncthreads();
+  const float NEG_INF = -__builtin_huge_valf();
+  for (int x = tid; x < G * kD; x += 256) {
+    const int h = x / kD, d = x - h * kD;
+    float M = NEG_INF;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) M = fmaxf(M, part_m[i >> 2][i & 3][h]);
+    float num = 0.f, den = 0.f;
+    if (M != NEG_INF) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float mi = part_m[i >> 2][i & 3][h];
+        const float wgt = (mi == NEG_INF) ? 0.f : fast_exp2(mi - M);
+        num += wgt * part_acc[i >> 2][i & 3][h][d];
+        den += wgt * part_l[i >> 2][i & 3][h];
+      }
+    }
+    part[h * head_stride + d] = num;
+    if (d == 0) {
+      part[h * head_stride + kD] = (den > 0.f) ? M : NEG_INF;
+      part[h * head_stride + kD + 1] = den;
+    }
   }
 }
 
 // Merge the split-K partials of one head: o = sum_c w_c o_c / sum_c w_c l_c
-// with w_c = exp2((m_c - M) * scale * log2 e), chunks in ascending order.
+// with w_c = exp2(m_c - M) (maxima are in log2 units), splits in ascending
+// order, so the result is bitwise reproducible.
 __global__ __launch_bounds__(128) void decode_combine(DecodeArgs a) {
   const int h = blockIdx.x;  // b * Hq + head
   const int d = threadIdx.x;
@@ -270,7 +302,7 @@ __global__ __launch_bounds__(128) void decode_combine(DecodeArgs a) {
     for (int c = 0; c < a.n_chunks; ++c) {
       const float mc = part[c * (kD + 2) + kD];
       if (mc == NEG_INF) continue;
-      const float w = fast_exp2((mc - M) * a.sl2);
+      const float w = fast_exp2(mc - M);
       num += w * part[c * (kD + 2) + d];
       den += w * part[c * (kD + 2) + kD + 1];
     }

@@ -63,11 +63,12 @@ struct DecodeArgs {
   int B, Hq, Hkv, cap, is_ring, local, window;
   int max_pos;            // clamp bound for positions
   int n_slots;            // cache slots scanned
-  int n_chunks;
+  int split;              // cache slots per split-K workgroup (multiple of 16)
+  int n_chunks;           // number of splits
   float base, inv_scale, sl2;
 };
 
-constexpr int kDecodeChunk = 256;  // cache slots per split-K workgroup
+constexpr int kDecodeChunk = 256;  // granularity of split-K decode splits (slots)
 
 hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, hipStream_t st);
 hipError_t launch_append_chunk(const AppendArgs& a, const Pos0Table& p0t, hipStream_t st);

@@ -33,13 +33,13 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_workspace_sizes(L):
-    assert L.g3attn_prefill_workspace_size(1, 8192, 32, 16, 128) == 16 * 8192 * 128 * 2 + 16 * 32 * 8 * 4
+    assert L.g3attn_prefill_workspace_size(1, 8192, 32, 16, 128) == 16 * 8192 * 128 * 2 + 16 * 64 * 8 * 4
     assert L.g3attn_prefill_workspace_size(0, 8192, 32, 16, 128) == 0
     ring = G.KVCacheC(0, 0, 1024, 1)
     lin = G.KVCacheC(0, 0, 40000, 0)
-    # ring: 4 chunks of 256 slots; linear: positions 0..32768 -> 129 chunks
+    # ring: 4 splits of 256 slots; linear: positions 0..32768 in splits of 4096 -> 9
     assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(ring)) == 32 * 32 * 4 * 130 * 4
-    assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(lin)) == 32 * 32 * 129 * 130 * 4
+    assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(lin)) == 32 * 32 * 9 * 130 * 4
 
 
 FAKE = 1 << 20  # a 16-byte aligned non-null address: validation fails before any use
