@@ -76,7 +76,12 @@ hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const Span
                           hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode(const DecodeArgs& a, int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// Flash prefill: waves per workgroup (each wave owns 32 query rows).
+#ifndef G3_PREFILL_WAVES
+#define G3_PREFILL_WAVES 8
+#endif
+constexpr int kPrefillWaves = G3_PREFILL_WAVES;
 // Tiles: positions per prefill workgroup for a GQA group of size G.
-inline int prefill_rows_per_wg(int G) { return 4 * (32 / G); }
+inline int prefill_rows_per_wg(int G) { return kPrefillWaves * (32 / G); }
 
 }  // namespace g3

@@ -177,11 +177,13 @@ __device__ __forceinline__ void tile_body(const uint16_t* kl, const uint16_t* vl
 // so one K/V tile in LDS serves all G heads.  Two workgroups fit on a CU
 // (<= 256 registers per wave), so every SIMD runs two independent waves and
 // one wave's softmax VALU work overlaps the other's MFMAs.
-template <int G, bool ONLINE>
-__global__ __launch_bounds__(256, 2)
+template <int G, bool ONLINE, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW)
 void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
-  constexpr int P = 32 / G;   // positions per wave
-  constexpr int WP = 4 * P;   // positions per workgroup
+  constexpr int P = 32 / G;    // positions per wave
+  constexpr int WP = NW * P;   // positions per workgroup
+  constexpr int NT = 64 * NW;  // threads per workgroup
+  constexpr int LR = 16 / NW;  // K (and V) rows each thread loads per tile
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kTileElemsK];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kTileElemsV];
   __shared__ double theta_rev[64];
@@ -241,23 +243,23 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   const int t_end = floor_div64(wg_hi - p0);  // inclusive
   const int n_t = t_end - t_begin + 1;
 
-  // ---- tile loader: thread -> 4 rows (16 threads per 256-byte row)
+  // ---- tile loader: 16 threads per 256-byte row, LR rows per thread
   const int ld_col = (tid & 15) * 8;
   const int ld_row = tid >> 4;
   const uint16_t* khat_head = a.khat + ((long long)b * a.Hkv + g) * a.S * kD + ld_col;
   const uint16_t* v_seq = a.v + ((long long)b * a.S * a.Hkv + g) * kD + ld_col;
   const long long vstride = (long long)a.Hkv * kD;
   const long long cache_off = ((long long)b * a.Hkv + g) * (long long)a.cap * kD + ld_col;
-  u32x4 pk[4], pv[4];
+  u32x4 pk[LR], pv[LR];
   // Branch-free: every lane always loads from a valid address (row 0 of this
   // head's chunk when its key does not exist) and zeroes the data after, so
   // all eight 16-byte loads of a tile are in flight together.
-  bool pvalid[4];
+  bool pvalid[LR];
   auto load_tile = [&](int t) {
     const int ts = p0 + t * kBN;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = ts + ld_row + 16 * u;
+    for (int u = 0; u < LR; ++u) {
+      const int j = ts + ld_row + (NT / 16) * u;
       const bool in_chunk = j >= p0 && j < chunk_end;
       const bool in_cache = a.has_cache && j < p0 && j >= kmin_avail;
       const int r = in_chunk ? j - p0 : 0;
@@ -276,8 +278,8 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   auto store_tile = [&](int buf) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = ld_row + 16 * u;
+    for (int u = 0; u < LR; ++u) {
+      const int row = ld_row + (NT / 16) * u;
       *(u32x4*)(&lds_k[buf][row * kLdsStrideK + ld_col]) = pvalid[u] ? pk[u] : zero;
       *(u32x4*)(&lds_v[buf][row * kLdsStrideV + ld_col]) = pvalid[u] ? pv[u] : zero;
     }
@@ -400,22 +402,24 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
 hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt, int G,
                           hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int grid = a.B * a.Hkv * a.n_qtiles;
+  constexpr int NW = kPrefillWaves;
+  const dim3 block(64 * NW);
   if (ev_start) hipEventRecord(ev_start, st);
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_fwd<1, false>), dim3(grid), dim3(256), 0, st, a, p0t, spt); break;
-    case 2: hipLaunchKernelGGL((prefill_fwd<2, false>), dim3(grid), dim3(256), 0, st, a, p0t, spt); break;
-    case 4: hipLaunchKernelGGL((prefill_fwd<4, false>), dim3(grid), dim3(256), 0, st, a, p0t, spt); break;
-    case 8: hipLaunchKernelGGL((prefill_fwd<8, false>), dim3(grid), dim3(256), 0, st, a, p0t, spt); break;
+    case 1: hipLaunchKernelGGL((prefill_fwd<1, false, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
+    case 2: hipLaunchKernelGGL((prefill_fwd<2, false, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
+    case 4: hipLaunchKernelGGL((prefill_fwd<4, false, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
+    case 8: hipLaunchKernelGGL((prefill_fwd<8, false, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (ev_stop) hipEventRecord(ev_stop, st);
   if (e != hipSuccess) return e;
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_fwd<1, true>), dim3(grid), dim3(256), 0, st, a, p0t, spt); break;
-    case 2: hipLaunchKernelGGL((prefill_fwd<2, true>), dim3(grid), dim3(256), 0, st, a, p0t, spt); break;
-    case 4: hipLaunchKernelGGL((prefill_fwd<4, true>), dim3(grid), dim3(256), 0, st, a, p0t, spt); break;
-    case 8: hipLaunchKernelGGL((prefill_fwd<8, true>), dim3(grid), dim3(256), 0, st, a, p0t, spt); break;
+    case 1: hipLaunchKernelGGL((prefill_fwd<1, true, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
+    case 2: hipLaunchKernelGGL((prefill_fwd<2, true, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
+    case 4: hipLaunchKernelGGL((prefill_fwd<4, true, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
+    case 8: hipLaunchKernelGGL((prefill_fwd<8, true, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
   }
   return hipGetLastError();
 }
