@@ -285,9 +285,8 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
     }
   };
 
-  load_tile(t_begin);
-  store_tile(0);
-  __syncthreads();  // also publishes theta_rev
+  load_tile(t_begin);  // in flight while Q is prepared
+  __syncthreads();     // publishes theta_rev
 
   // ---- Q prologue: load, QK-RMSNorm, RoPE, scale by softmax_scale * log2(e),
   // round to bf16: the B operand of S^T = K Q^T (lane: query ln, dims
@@ -340,6 +339,9 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
       qreg[s] = __builtin_bit_cast(bf16x8, wv);
     }
   }
+
+  store_tile(0);
+  __syncthreads();
 
   const int tr_g = lane >> 4;
   const int tr_w = lane & 15;
