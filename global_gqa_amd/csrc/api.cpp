@@ -56,6 +56,15 @@ int check_scale(float softmax_scale, float* sl2) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// RoPE frequencies base^(-2k/D), in revolutions per (interpolated) position.
+g3::RopeTable rope_table(float base, float interp_scale) {
+  g3::RopeTable t;
+  const double inv2pi = 0.15915494309189533576888376337251;
+  for (int k = 0; k < g3::kD / 2; ++k)
+    t.rev[k] = std::pow((double)base, -2.0 * k / g3::kD) * inv2pi / (double)interp_scale;
+  return t;
+}
+
 // Prefill workspace: normed+rotated chunk keys [B][Hkv][S][D] bf16, then one
 // int32 flag per flash workgroup (sized for the smallest tile, G = 1).
 size_t prefill_ws_keys(int32_t B, int32_t S, int32_t Hkv, int32_t D) {
@@ -142,9 +151,7 @@ int g3attn_qknorm_rope(const g3_bf16* q_in, const g3_bf16* k_in, g3_bf16* q_out,
     a.H = which ? Hkv : Hq;
     a.S = T;
     a.head_major = 0;
-    a.base = rope_base;
-    a.inv_scale = 1.0f / interp_scale;
-    if (hipError_t e = g3::launch_qknorm_rope(a, p0t, st))
+    if (hipError_t e = g3::launch_qknorm_rope(a, p0t, rope_table(rope_base, interp_scale), st))
       return fail(G3_EHIP, "qknorm_rope launch failed: %s", hipGetErrorString(e));
   }
   return G3_OK;
@@ -232,6 +239,7 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
 
   hipStream_t st = (hipStream_t)stream;
   uint16_t* khat = (uint16_t*)workspace;
+  const g3::RopeTable rt = rope_table(rope_base, interp_scale);
   {
     g3::RowsArgs a{};
     a.in = k;
@@ -243,9 +251,7 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
     a.H = Hkv;
     a.S = S;
     a.head_major = 1;
-    a.base = rope_base;
-    a.inv_scale = 1.0f / interp_scale;
-    if (hipError_t e = g3::launch_qknorm_rope(a, p0t, st))
+    if (hipError_t e = g3::launch_qknorm_rope(a, p0t, rt, st))
       return fail(G3_EHIP, "k prologue launch failed: %s", hipGetErrorString(e));
   }
   const int G = Hq / Hkv;
@@ -268,13 +274,11 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
   a.has_cache = cache ? 1 : 0;
   a.local = layer_kind == G3_LOCAL;
   a.window = layer_kind == G3_LOCAL ? window : (1 << 30);
-  a.base = rope_base;
-  a.inv_scale = 1.0f / interp_scale;
   a.sl2 = sl2;
   const int rows = g3::prefill_rows_per_wg(G);
   a.n_qtiles = (S + rows - 1) / rows;
   if ((long long)B * Hkv * a.n_qtiles > (1LL << 31) - 1) return fail(G3_EINVAL, "grid too large");
-  if (hipError_t e = g3::launch_prefill(a, p0t, spt, G, st, g_ev_start, g_ev_stop))
+  if (hipError_t e = g3::launch_prefill(a, p0t, spt, rt, G, st, g_ev_start, g_ev_stop))
     return fail(G3_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
   if (cache) {
     g3::AppendArgs ap{};
@@ -358,10 +362,9 @@ int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, 
   a.n_slots = n_slots;
   a.split = split;
   a.n_chunks = n_chunks;
-  a.base = rope_base;
-  a.inv_scale = 1.0f / interp_scale;
   a.sl2 = sl2;
-  if (hipError_t e = g3::launch_decode(a, Hq / Hkv, (hipStream_t)stream, g_ev_start, g_ev_stop))
+  if (hipError_t e = g3::launch_decode(a, rope_table(rope_base, interp_scale), Hq / Hkv, (hipStream_t)stream,
+                                       g_ev_start, g_ev_stop))
     return fail(G3_EHIP, "decode launch failed: %s", hipGetErrorString(e));
   return G3_OK;
 }

@@ -35,7 +35,7 @@ __device__ __forceinline__ float wave_max(float x) {
 
 // RMSNorm + RoPE of one raw 128-vector by one wave: lane owns (k, k + 64).
 __device__ __forceinline__ void norm_rope_vec(const uint16_t* src, const float* gamma, float eps, int pos,
-                                              float base, float inv_scale, int lane, float& y0, float& y1) {
+                                              double rev, int lane, float& y0, float& y1) {
   float x0 = __uint_as_float((uint32_t)src[lane] << 16);
   float x1 = __uint_as_float((uint32_t)src[lane + 64] << 16);
   if (gamma) {
@@ -45,7 +45,7 @@ __device__ __forceinline__ void norm_rope_vec(const uint16_t* src, const float* 
     x1 *= rn * gamma[lane + 64];
   }
   float sn, cs;
-  rope_sincos(pos, rope_rev_freq(lane, base, inv_scale), sn, cs);
+  rope_sincos(pos, rev, sn, cs);
   y0 = x0 * cs - x1 * sn;
   y1 = x0 * sn + x1 * cs;
 }
@@ -164,7 +164,7 @@ __device__ __forceinline__ void stream_split(const DecodeArgs& a, const float (&
 }
 
 template <int G>
-__global__ __launch_bounds__(256) void decode_splitk(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_splitk(DecodeArgs a, RopeTable rt) {
   __shared__ float kn[kD];
   __shared__ float vn[kD];
   __shared__ float part_m[4][4][G];            // [wave][key group][head]
@@ -210,15 +210,14 @@ __global__ __launch_bounds__(256) void decode_splitk(DecodeArgs a) {
     __shared__ float qh[G][kD];
     for (int hg = wave; hg < G; hg += 4) {
       float y0, y1;
-      norm_rope_vec(a.q + ((long long)b * a.Hq + g * G + hg) * kD, a.q_gamma, a.eps, p, a.base, a.inv_scale,
-                    lane, y0, y1);
+      norm_rope_vec(a.q + ((long long)b * a.Hq + g * G + hg) * kD, a.q_gamma, a.eps, p, rt.rev[lane], lane, y0, y1);
       qh[hg][lane] = round_bf16(y0 * a.sl2);
       qh[hg][lane + 64] = round_bf16(y1 * a.sl2);
     }
     if (owner && wave == 3) {
       float y0, y1;
       const long long src = ((long long)b * a.Hkv + g) * kD;
-      norm_rope_vec(a.k_new + src, a.k_gamma, a.eps, p, a.base, a.inv_scale, lane, y0, y1);
+      norm_rope_vec(a.k_new + src, a.k_gamma, a.eps, p, rt.rev[lane], lane, y0, y1);
       const uint32_t w = pack2(y0, y1);
       kn[lane] = bf_lo(w);
       kn[lane + 64] = bf_hi(w);
@@ -311,14 +310,15 @@ __global__ __launch_bounds__(128) void decode_combine(DecodeArgs a) {
   a.o[(long long)h * kD + d] = (uint16_t)(pack2(o, 0.f) & 0xffffu);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
+hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start,
+                         hipEvent_t ev_stop) {
   const dim3 grid(a.n_chunks, a.B * a.Hkv);
   if (ev_start) hipEventRecord(ev_start, st);
   switch (G) {
-    case 1: hipLaunchKernelGGL(decode_splitk<1>, grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(decode_splitk<2>, grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(decode_splitk<4>, grid, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL(decode_splitk<8>, grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL(decode_splitk<1>, grid, dim3(256), 0, st, a, rt); break;
+    case 2: hipLaunchKernelGGL(decode_splitk<2>, grid, dim3(256), 0, st, a, rt); break;
+    case 4: hipLaunchKernelGGL(decode_splitk<4>, grid, dim3(256), 0, st, a, rt); break;
+    case 8: hipLaunchKernelGGL(decode_splitk<8>, grid, dim3(256), 0, st, a, rt); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

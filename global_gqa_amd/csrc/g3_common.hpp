@@ -39,6 +39,12 @@ struct Pos0Table {
 
 __device__ __forceinline__ int pos0_of(const Pos0Table& t, int b) { return t.uniform ? t.v[0] : t.v[b]; }
 
+// RoPE frequencies of the 64 rotation pairs in revolutions per position,
+// base^(-2k/D) / (2 pi) / interp_scale, computed once per call in fp64.
+struct RopeTable {
+  double rev[kD / 2];
+};
+
 // bf16 <-> f32 on packed 32-bit words (low half = element 0).
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -48,13 +54,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {  // round to neare
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// RoPE frequency of pair k in revolutions per (interpolated) position:
-// base^(-2k/D) / (2 pi) / interp_scale, evaluated in fp64.
-__device__ __forceinline__ double rope_rev_freq(int k, float base, float inv_scale) {
-  const double inv2pi = 0.15915494309189533576888376337251;
-  return exp2(-(2.0 * k / kD) * log2((double)base)) * inv2pi * (double)inv_scale;
-}
 
 // sin/cos of 2*pi*(pos * rev): the product is reduced to [-1/2, 1/2]
 // revolutions in fp64 before the fp32 hardware sin/cos (which take

@@ -19,7 +19,6 @@ struct RowsArgs {
   float eps;
   int T, H, S;            // S: tokens per sequence (for pos0 and head-major)
   int head_major;
-  float base, inv_scale;
 };
 
 struct AppendArgs {
@@ -43,7 +42,6 @@ struct PrefillArgs {
   int B, S, Hq, Hkv;
   int cap, is_ring, has_cache;
   int local, window;
-  float base, inv_scale;
   float sl2;              // softmax_scale * log2(e)
   int n_qtiles;
 };
@@ -65,16 +63,17 @@ struct DecodeArgs {
   int n_slots;            // cache slots scanned
   int split;              // cache slots per split-K workgroup (multiple of 16)
   int n_chunks;           // number of splits
-  float base, inv_scale, sl2;
+  float sl2;
 };
 
 constexpr int kDecodeChunk = 256;  // granularity of split-K decode splits (slots)
 
-hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, hipStream_t st);
+hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st);
 hipError_t launch_append_chunk(const AppendArgs& a, const Pos0Table& p0t, hipStream_t st);
-hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt, int G,
-                          hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
-hipError_t launch_decode(const DecodeArgs& a, int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt, const RopeTable& rt,
+                          int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start,
+                         hipEvent_t ev_stop);
 
 // Flash prefill: waves per workgroup (each wave owns 32 query rows).
 #ifndef G3_PREFILL_WAVES

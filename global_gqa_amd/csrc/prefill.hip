@@ -11,10 +11,10 @@
 // contiguous range [lo(i), hi(i)], so tiles outside the union of the rows'
 // ranges are never loaded ("window-aware tile skipping").
 //
-// Design (per workgroup = 4 waves, one (sequence, kv head, query tile)):
-//   * GQA packing: each wave owns 64 query rows = (64/G positions) x (G heads
-//     of one kv group), so one K/V tile in LDS feeds 64 rows per wave.
-//   * Q is loaded once, QK-RMSNorm + RoPE are applied in registers (fp64
+// Design (per workgroup = 8 waves, one (sequence, kv head, query tile)):
+//   * GQA packing: each wave owns 32 query rows = (32/G positions) x (G heads
+//     of one kv group), so one K/V tile in LDS feeds 256 rows per workgroup.
+//   * Q is loaded once (whole rows, through LDS), QK-RMSNorm + RoPE are applied in registers (fp64
 //     angle reduction), and Q stays in VGPRs as the B operand of
 //     S^T = K Q^T (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  Computing
 //     S transposed puts one query per lane, so row max / row sum are
@@ -65,6 +65,14 @@ __device__ __forceinline__ float xhalf_max(float x) {
 __device__ __forceinline__ float xhalf_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes of
+// the same wave (LDS instructions of one wave execute in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ int floor_div64(int x) { return x >= 0 ? x / 64 : -((63 - x) / 64); }
@@ -172,21 +180,27 @@ __device__ __forceinline__ void tile_body(const uint16_t* kl, const uint16_t* vl
 
 }  // namespace
 
-// Workgroup = 4 waves = one (sequence, kv head, query tile).  Each wave owns
+// Workgroup = NW waves = one (sequence, kv head, query tile).  Each wave owns
 // 32 query rows: 32/G positions x the G query heads that share the kv head,
-// so one K/V tile in LDS serves all G heads.  Two workgroups fit on a CU
-// (<= 256 registers per wave), so every SIMD runs two independent waves and
-// one wave's softmax VALU work overlaps the other's MFMAs.
+// so one K/V tile in LDS serves all G heads and all NW waves.  With NW = 8
+// one workgroup fills a CU (two waves per SIMD): one wave's softmax VALU
+// work overlaps the other's MFMAs, and each K/V tile crosses L2 -> LDS once
+// per 256 query rows.
 template <int G, bool ONLINE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW)
-void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
+void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   constexpr int P = 32 / G;    // positions per wave
   constexpr int WP = NW * P;   // positions per workgroup
   constexpr int NT = 64 * NW;  // threads per workgroup
   constexpr int LR = 16 / NW;  // K (and V) rows each thread loads per tile
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kTileElemsK];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kTileElemsV];
-  __shared__ double theta_rev[64];
+  // One LDS block, laid out by hand: the double-buffered K and V tiles first
+  // (their addresses stay below 64 KiB, within ds_* immediate offsets), then
+  // each wave's staging rows for its 32 Q rows (prologue) and O rows
+  // (epilogue), so both move between HBM and registers as whole 256-byte rows.
+  constexpr int kTiles = 2 * kTileElemsK + 2 * kTileElemsV;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kTiles + NW * 32 * kLdsStrideK];
+  auto lds_k = [&](int buf) { return lds + buf * kTileElemsK; };
+  auto lds_v = [&](int buf) { return lds + 2 * kTileElemsK + buf * kTileElemsV; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -205,43 +219,44 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   const int chunk_end = p0 + a.S;
   const int kmin_avail = a.has_cache ? (a.is_ring ? max(0, p0 - a.cap) : 0) : p0;
   const int qbase = p0 + qt * WP;  // first query position of the workgroup
+  const int wbase = qbase + wave * P;  // first query position of this wave
 
-  if (tid < 64) theta_rev[tid] = rope_rev_freq(tid, a.base, a.inv_scale);
-
-  // ---- key ranges: whole workgroup (tiles to stream) and this wave
-  int wg_lo = 0x7fffffff, wg_hi = -0x7fffffff;
+  // ---- Q rows of this wave, loaded row-major: 16 lanes x 16 B per row.
+  // Staging row x = (head hg, position offset u) is x = hg * P + u.
+  uint16_t* xs = lds + kTiles + wave * 32 * kLdsStrideK;
+  const int x_col = (lane & 15) * 8;
+  {
+    u32x4 qv[8];
 #pragma unroll
-  for (int k = 0; k < (WP + 63) / 64; ++k) {
-    const int idx = lane + 64 * k;
-    const int i = qbase + idx;
-    if (idx < WP && i < chunk_end) {
-      const RowRange r = row_range(i, b, kmin_avail, a, spt);
-      wg_lo = min(wg_lo, r.lo);
-      wg_hi = max(wg_hi, r.hi);
+    for (int k = 0; k < 8; ++k) {
+      const int x = 4 * k + (lane >> 4);
+      const int hg = x / P, u = x - (x / P) * P;
+      const int pos = wbase + u;
+      const int r = pos < chunk_end ? pos - p0 : 0;  // valid address; rows past the end are never stored
+      qv[k] = *(const u32x4*)(a.q + (((long long)b * a.S + r) * a.Hq + g * G + hg) * kD + x_col);
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) *(u32x4*)(xs + (4 * k + (lane >> 4)) * kLdsStrideK + x_col) = qv[k];
   }
-  wg_lo = wave_min_i(wg_lo);
-  wg_hi = wave_max_i(wg_hi);
 
-  // this lane's query row: position offset ln % P, head ln / P of the group
-  const int hg = ln / P;
-  const int row_pos = qbase + wave * P + (ln - hg * P);
-  const int row_head = g * G + hg;
-  const bool row_ok = row_pos < chunk_end;
-  int row_lo = 0x7fffffff, row_hi = -0x7fffffff;
-  if (row_ok) {
-    const RowRange rr = row_range(row_pos, b, kmin_avail, a, spt);
-    row_lo = rr.lo;
-    row_hi = rr.hi;
-  }
-  const int w_lo_min = wave_min_i(row_ok ? row_lo : 0x7fffffff);
-  const int w_hi_max = wave_max_i(row_ok ? row_hi : -0x7fffffff);
-  const int w_lo_max = wave_max_i(row_ok ? row_lo : -0x7fffffff);
-  const int w_hi_min = wave_min_i(row_ok ? row_hi : 0x7fffffff);
-
-  const int t_begin = floor_div64(wg_lo - p0);
-  const int t_end = floor_div64(wg_hi - p0);  // inclusive
+  // ---- key ranges.  lo(i) and hi(i) are non-decreasing in i, so the union
+  // over a run of rows is [lo(first), hi(last)] and the intersection is
+  // [lo(last), hi(first)].
+  const int wg_last = min(qbase + WP, chunk_end) - 1;
+  const RowRange wg_first_r = row_range(qbase, b, kmin_avail, a, spt);
+  const RowRange wg_last_r = row_range(wg_last, b, kmin_avail, a, spt);
+  const int t_begin = floor_div64(wg_first_r.lo - p0);
+  const int t_end = floor_div64(wg_last_r.hi - p0);  // inclusive
   const int n_t = t_end - t_begin + 1;
+  int w_lo_min = 0x7fffffff, w_hi_max = -0x7fffffff, w_lo_max = 0x7fffffff, w_hi_min = -0x7fffffff;
+  if (wbase < chunk_end) {
+    const RowRange f = row_range(wbase, b, kmin_avail, a, spt);
+    const RowRange l = row_range(min(wbase + P, chunk_end) - 1, b, kmin_avail, a, spt);
+    w_lo_min = f.lo;
+    w_hi_min = f.hi;
+    w_lo_max = l.lo;
+    w_hi_max = l.hi;
+  }
 
   // ---- tile loader: 16 threads per 256-byte row, LR rows per thread
   const int ld_col = (tid & 15) * 8;
@@ -253,7 +268,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
   u32x4 pk[LR], pv[LR];
   // Branch-free: every lane always loads from a valid address (row 0 of this
   // head's chunk when its key does not exist) and zeroes the data after, so
-  // all eight 16-byte loads of a tile are in flight together.
+  // all of a tile's 16-byte loads are in flight together.
   bool pvalid[LR];
   auto load_tile = [&](int t) {
     const int ts = p0 + t * kBN;
@@ -280,34 +295,40 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
 #pragma unroll
     for (int u = 0; u < LR; ++u) {
       const int row = ld_row + (NT / 16) * u;
-      *(u32x4*)(&lds_k[buf][row * kLdsStrideK + ld_col]) = pvalid[u] ? pk[u] : zero;
-      *(u32x4*)(&lds_v[buf][row * kLdsStrideV + ld_col]) = pvalid[u] ? pv[u] : zero;
+      *(u32x4*)(lds_k(buf) + row * kLdsStrideK + ld_col) = pvalid[u] ? pk[u] : zero;
+      *(u32x4*)(lds_v(buf) + row * kLdsStrideV + ld_col) = pvalid[u] ? pv[u] : zero;
     }
   };
 
   load_tile(t_begin);  // in flight while Q is prepared
-  __syncthreads();     // publishes theta_rev
 
-  // ---- Q prologue: load, QK-RMSNorm, RoPE, scale by softmax_scale * log2(e),
+  // this lane's query row: position offset ln % P, head ln / P of the group
+  const int hg = ln / P;
+  const int row_pos = wbase + (ln - hg * P);
+  const int row_head = g * G + hg;
+  const bool row_ok = row_pos < chunk_end;
+  int row_lo = 0x7fffffff, row_hi = -0x7fffffff;
+  if (row_ok) {
+    const RowRange rr = row_range(row_pos, b, kmin_avail, a, spt);
+    row_lo = rr.lo;
+    row_hi = rr.hi;
+  }
+
+  // ---- Q prologue: QK-RMSNorm, RoPE, scale by softmax_scale * log2(e),
   // round to bf16: the B operand of S^T = K Q^T (lane: query ln, dims
   // 16 s + 8 h2 + [0, 8)), so scores come out in log2 units.
+  wave_lds_sync();
   bf16x8 qreg[8];
   {
     float x[64];
-    if (row_ok) {
-      const uint16_t* src = a.q + (((long long)b * a.S + (row_pos - p0)) * a.Hq + row_head) * kD + 8 * h2;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const u32x4 wv = *(const u32x4*)(src + 16 * s);
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 wv = *(const u32x4*)(xs + ln * kLdsStrideK + 16 * s + 8 * h2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[8 * s + 2 * e] = bf_lo(wv[e]);
-          x[8 * s + 2 * e + 1] = bf_hi(wv[e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        x[8 * s + 2 * e] = bf_lo(wv[e]);
+        x[8 * s + 2 * e + 1] = bf_hi(wv[e]);
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 64; ++e) x[e] = 0.f;
     }
     float rn = a.sl2;
     if (a.q_gamma) {
@@ -325,8 +346,9 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        const double rev = rt.rev[16 * s + 8 * h2 + e];
         float sn, cs;
-        rope_sincos(row_pos, theta_rev[16 * s + 8 * h2 + e], sn, cs);
+        rope_sincos(row_pos, rev, sn, cs);
         const float x1 = x[8 * s + e] * rn, x2 = x[8 * (s + 4) + e] * rn;
         x[8 * s + e] = x1 * cs - x2 * sn;
         x[8 * (s + 4) + e] = x1 * sn + x2 * cs;
@@ -363,9 +385,9 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
     const int ts = p0 + t * kBN;
     if (ts <= w_hi_max && ts + kBN - 1 >= w_lo_min) {
       if (ts >= w_lo_max && ts + kBN - 1 <= w_hi_min)
-        tile_body<false, ONLINE>(lds_k[cur], lds_v[cur], qreg, ws, row_lo, row_hi, ts, ln, h2, tr_off);
+        tile_body<false, ONLINE>(lds_k(cur), lds_v(cur), qreg, ws, row_lo, row_hi, ts, ln, h2, tr_off);
       else
-        tile_body<true, ONLINE>(lds_k[cur], lds_v[cur], qreg, ws, row_lo, row_hi, ts, ln, h2, tr_off);
+        tile_body<true, ONLINE>(lds_k(cur), lds_v(cur), qreg, ws, row_lo, row_hi, ts, ln, h2, tr_off);
     }
     if (it + 1 < n_t) store_tile(cur ^ 1);
     __syncthreads();
@@ -385,43 +407,57 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt) {
     if (any_bad) return;
   }
 
-  // ---- epilogue: O / l, bf16, store the row [b][pos][head][dims]
-  if (row_ok) {
-    const float inv = 1.f / lt;
-    uint16_t* dst = a.o + (((long long)b * a.S + (row_pos - p0)) * a.Hq + row_head) * kD;
+  // ---- epilogue: O / l to bf16 into the wave's staging rows, then whole
+  // 256-byte rows out to [b][pos][head][dims]
+  {
+    const float inv = row_ok ? 1.f / lt : 0.f;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * mb + 8 * q4 + 4 * h2;
         const f32x16& oa = ws.o[mb];
-        *(u32x2*)(dst + d) = u32x2{pack2(oa[4 * q4] * inv, oa[4 * q4 + 1] * inv),
-                                   pack2(oa[4 * q4 + 2] * inv, oa[4 * q4 + 3] * inv)};
+        *(u32x2*)(xs + ln * kLdsStrideK + d) = u32x2{pack2(oa[4 * q4] * inv, oa[4 * q4 + 1] * inv),
+                                                     pack2(oa[4 * q4 + 2] * inv, oa[4 * q4 + 3] * inv)};
       }
+  }
+  wave_lds_sync();
+  // An opaque copy of the lane index keeps the compiler from carrying the Q
+  // prologue's row addresses (same offsets) through the tile loop.
+  int el = lane;
+  asm volatile("" : "+v"(el));
+  const int e_col = (el & 15) * 8;
+  uint16_t* o_wave = a.o + (((long long)b * a.S + (wbase - p0)) * a.Hq + g * G) * kD;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int x = 4 * k + (el >> 4);
+    const int xh = x / P, u = x - (x / P) * P;
+    const u32x4 ov = *(const u32x4*)(xs + x * kLdsStrideK + e_col);
+    if (wbase + u < chunk_end) *(u32x4*)(o_wave + (u * a.Hq + xh) * kD + e_col) = ov;
   }
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt, int G,
-                          hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
+hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt, const RopeTable& rt,
+                          int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int grid = a.B * a.Hkv * a.n_qtiles;
   constexpr int NW = kPrefillWaves;
   const dim3 block(64 * NW);
   if (ev_start) hipEventRecord(ev_start, st);
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_fwd<1, false, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
-    case 2: hipLaunchKernelGGL((prefill_fwd<2, false, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
-    case 4: hipLaunchKernelGGL((prefill_fwd<4, false, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
-    case 8: hipLaunchKernelGGL((prefill_fwd<8, false, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
+    case 1: hipLaunchKernelGGL((prefill_fwd<1, false, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
+    case 2: hipLaunchKernelGGL((prefill_fwd<2, false, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
+    case 4: hipLaunchKernelGGL((prefill_fwd<4, false, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
+    case 8: hipLaunchKernelGGL((prefill_fwd<8, false, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (ev_stop) hipEventRecord(ev_stop, st);
   if (e != hipSuccess) return e;
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_fwd<1, true, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
-    case 2: hipLaunchKernelGGL((prefill_fwd<2, true, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
-    case 4: hipLaunchKernelGGL((prefill_fwd<4, true, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
-    case 8: hipLaunchKernelGGL((prefill_fwd<8, true, NW>), dim3(grid), block, 0, st, a, p0t, spt); break;
+    case 1: hipLaunchKernelGGL((prefill_fwd<1, true, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
+    case 2: hipLaunchKernelGGL((prefill_fwd<2, true, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
+    case 4: hipLaunchKernelGGL((prefill_fwd<4, true, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
+    case 8: hipLaunchKernelGGL((prefill_fwd<8, true, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
   }
   return hipGetLastError();
 }

@@ -15,15 +15,11 @@ namespace g3 {
 // 16 lanes per head row; lane j owns dims [4j, 4j+4) and [64+4j, 64+4j+4),
 // so every rotation pair stays inside one lane.
 template <bool NORM>
-__global__ __launch_bounds__(256) void qknorm_rope_rows(RowsArgs a, Pos0Table p0t) {
+__global__ __launch_bounds__(256) void qknorm_rope_rows(RowsArgs a, Pos0Table p0t, RopeTable rt) {
   const int j = threadIdx.x & 15;
-  // the 64 rotation frequencies, computed once per workgroup in fp64
-  __shared__ double freq[64];
-  if (threadIdx.x < 64) freq[threadIdx.x] = rope_rev_freq(threadIdx.x, a.base, a.inv_scale);
-  __syncthreads();
   double rev[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rev[i] = freq[4 * j + i];
+  for (int i = 0; i < 4; ++i) rev[i] = rt.rev[4 * j + i];
   float gam[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -98,14 +94,14 @@ static int grid_for(long long work_items, int per_block) {
   return (int)g;
 }
 
-hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, hipStream_t st) {
+hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st) {
   // a grid-stride loop over rows: at most 8 workgroups per CU
   long long grid = ((long long)a.T * a.H + 15) / 16;
   if (grid > 2048) grid = 2048;
   if (a.gamma)
-    hipLaunchKernelGGL(qknorm_rope_rows<true>, dim3((int)grid), dim3(256), 0, st, a, p0t);
+    hipLaunchKernelGGL(qknorm_rope_rows<true>, dim3((int)grid), dim3(256), 0, st, a, p0t, rt);
   else
-    hipLaunchKernelGGL(qknorm_rope_rows<false>, dim3((int)grid), dim3(256), 0, st, a, p0t);
+    hipLaunchKernelGGL(qknorm_rope_rows<false>, dim3((int)grid), dim3(256), 0, st, a, p0t, rt);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_workspace_sizes(L):
-    assert L.g3attn_prefill_workspace_size(1, 8192, 32, 16, 128) == 16 * 8192 * 128 * 2 + 16 * 64 * 8 * 4
+    assert L.g3attn_prefill_workspace_size(1, 8192, 32, 16, 128) == 16 * 8192 * 128 * 2 + 16 * 32 * 8 * 4
     assert L.g3attn_prefill_workspace_size(0, 8192, 32, 16, 128) == 0
     ring = G.KVCacheC(0, 0, 1024, 1)
     lin = G.KVCacheC(0, 0, 40000, 0)
