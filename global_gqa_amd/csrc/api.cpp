@@ -180,6 +180,9 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
   for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o})
     if (!aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
   if ((long long)B * S * Hq > (1LL << 31) - 1) return fail(G3_EINVAL, "B*S*Hq too large");
+  if ((long long)S * Hkv * D > (1LL << 31) - 1)
+    return fail(G3_EUNSUPPORTED, "S*Hkv*D=%lld exceeds the 32-bit row offsets of one sequence",
+                (long long)S * Hkv * D);
 
   g3::Pos0Table p0t{};
   p0t.uniform = 1;

@@ -37,12 +37,15 @@ namespace g3 {
 namespace {
 
 constexpr int kBN = 64;           // keys per LDS tile (two halves of 32)
-// LDS row strides (bf16 elements).  K rows are read 16 B per lane by 32
-// lanes of different rows (S^T A operand): 256 + 16 B spreads 8 consecutive
-// rows over all 32 banks.  V rows are read by ds_read_b64_tr_b16 in groups of
-// 16 lanes covering 4 rows x 32 B: 256 + 32 B puts those rows on disjoint banks.
+// LDS row strides (bf16 elements), chosen by measured read rate on gfx950
+// (64 banks of 4 bytes).  K rows are read 16 B per lane by 32 lanes of
+// different rows (S^T A operand): 256 + 16 B per row runs at the full LDS
+// rate.  V rows are read by ds_read_b64_tr_b16, each 16-lane group covering
+// 4 rows x 32 B and two groups 4 rows x 64 B: 256 + 64 B per row puts the
+// rows a 32-lane half touches on disjoint banks (256 + 32 B conflicts 2-way
+// on half of them).
 constexpr int kLdsStrideK = 136;
-constexpr int kLdsStrideV = 144;
+constexpr int kLdsStrideV = 160;
 constexpr int kTileElemsK = kBN * kLdsStrideK;
 constexpr int kTileElemsV = kBN * kLdsStrideV;
 
@@ -103,15 +106,13 @@ struct WaveState {
   float m;       // running max (log2 units), online-maximum pass only
 };
 
-// One 64-key tile for one wave of 32 query rows:
-//   S^T (64 keys x 32 queries) = K Q^T      16 MFMA 32x32x16, K from LDS
-//   p = exp2(S) (scores are already in log2 units; masked keys -> 0)
-//   O^T (128 dims x 32 queries) += V^T P^T  16 MFMA, V^T via transposing reads
-template <bool MASK, bool ONLINE>
-__device__ __forceinline__ void tile_body(const uint16_t* kl, const uint16_t* vl, const bf16x8 (&q)[8],
-                                          WaveState& w, int lo, int hi, int ts, int ln, int h2, int tr_off) {
-  const float NEG_INF = -__builtin_huge_valf();
-  f32x16 s[2];
+// One 64-key tile for one wave of 32 query rows, in three steps:
+//   qk:      S^T (64 keys x 32 queries) = K Q^T, 16 MFMA 32x32x16, K from LDS
+//   softmax: p = exp2(S) (scores are already in log2 units; masked keys -> 0),
+//            row sums, p packed to bf16 as the B operand of P V
+//   pv:      O^T (128 dims x 32 queries) += V^T P^T, 16 MFMA, V^T through
+//            transposing LDS reads
+__device__ __forceinline__ void qk(const uint16_t* kl, const bf16x8 (&q)[8], f32x16 (&s)[2], int ln, int h2) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -123,6 +124,12 @@ __device__ __forceinline__ void tile_body(const uint16_t* kl, const uint16_t* vl
       const bf16x8 kop = *(const bf16x8*)(kl + (kb * 32 + ln) * kLdsStrideK + 16 * st + 8 * h2);
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[st], s[kb], 0, 0, 0);
     }
+}
+
+template <bool MASK, bool ONLINE>
+__device__ __forceinline__ void softmax(f32x16 (&s)[2], WaveState& w, bf16x8 (&pb)[4], int lo, int hi, int ts,
+                                        int h2) {
+  const float NEG_INF = -__builtin_huge_valf();
   if (MASK) {
     // key of (kb, r) = ts + 32 kb + 8 (r / 4) + 4 h2 + r % 4
 #pragma unroll
@@ -151,7 +158,6 @@ __device__ __forceinline__ void tile_body(const uint16_t* kl, const uint16_t* vl
 #pragma unroll
       for (int r = 0; r < 16; ++r) w.o[mb][r] *= alpha;
   }
-  bf16x8 pb[4];
   float rs = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -166,16 +172,132 @@ __device__ __forceinline__ void tile_body(const uint16_t* kl, const uint16_t* vl
     pb[t] = __builtin_bit_cast(bf16x8, u);
   }
   w.l += rs;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
+}
+
+__device__ __forceinline__ void pv(const uint16_t* vl, const bf16x8 (&pb)[4], WaveState& w, int tr_off) {
+  // V^T operands of 16-key step t are read one step ahead of their MFMAs
+  bf16x8 vop[2][4];
+  auto read_step = [&](int t, bf16x8 (&dst)[4]) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const uint16_t* base = vl + 16 * t * kLdsStrideV + 32 * mb + tr_off;
       const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
       const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * kLdsStrideV));
-      const bf16x8 vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      w.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[t], w.o[mb], 0, 0, 0);
+      dst[mb] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+  };
+  read_step(0, vop[0]);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t < 3) read_step(t + 1, vop[(t + 1) & 1]);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      w.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t & 1][mb], pb[t], w.o[mb], 0, 0, 0);
+  }
+}
+
+// The matrix half of a tile step: PV of the previous tile (if DO_PV) then QK
+// of this one (if DO_QK), 16 + 16 MFMAs.  LDS operand reads run two PV steps
+// (256 MFMA cycles) or four QK steps ahead of the MFMAs that use them, and
+// scheduling fences keep the compiler from pulling them back next to their
+// uses, where each MFMA would wait out a full LDS latency.
+template <bool DO_PV, bool DO_QK>
+__device__ __forceinline__ void gemm_half(const uint16_t* vl, const uint16_t* kl, const bf16x8 (&pb)[4],
+                                          const bf16x8 (&q)[8], f32x16 (&s)[2], WaveState& w, int ln, int h2,
+                                          int tr_off) {
+  bf16x8 vop[4][4];  // [16-key step][dim block]
+  bf16x8 kop[8][2];  // [16-dim step][key half]
+  auto rd_v = [&](int t) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const uint16_t* base = vl + 16 * t * kLdsStrideV + 32 * mb + tr_off;
+      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
+      const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * kLdsStrideV));
+      vop[t][mb] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto rd_k = [&](int st) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      kop[st][kb] = *(const bf16x8*)(kl + (kb * 32 + ln) * kLdsStrideK + 16 * st + 8 * h2);
+  };
+  auto mm_pv = [&](int t) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      w.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][mb], pb[t], w.o[mb], 0, 0, 0);
+  };
+  auto mm_qk = [&](int st) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[st][kb], q[st], s[kb], 0, 0, 0);
+  };
+  auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
+  if (DO_QK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+  }
+  constexpr int KA = DO_PV ? 6 : 4;  // K steps read before the first QK MFMA
+  if (DO_PV) {
+    rd_v(0);
+    rd_v(1);
+  }
+  if (DO_QK) {
+    rd_k(0);
+    rd_k(1);
+  }
+  fence();
+  if (DO_PV) {
+    mm_pv(0);
+    rd_v(2);
+    fence();
+    mm_pv(1);
+    rd_v(3);
+    fence();
+    mm_pv(2);
+    if (DO_QK) {
+      rd_k(2);
+      rd_k(3);
+    }
+    fence();
+    mm_pv(3);
+    if (DO_QK) {
+      rd_k(4);
+      rd_k(5);
+    }
+    fence();
+  } else if (DO_QK) {
+    rd_k(2);
+    rd_k(3);
+    fence();
+  }
+  if (DO_QK) {
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      mm_qk(st);
+      if (st + KA < 8) rd_k(st + KA);
+      fence();
+    }
+  }
+}
+
+template <bool DO_PV>
+__device__ __forceinline__ void gemm_step(bool do_qk, const uint16_t* vl, const uint16_t* kl, const bf16x8 (&pb)[4],
+                                          const bf16x8 (&q)[8], f32x16 (&s)[2], WaveState& w, int ln, int h2,
+                                          int tr_off) {
+  if (do_qk)
+    gemm_half<DO_PV, true>(vl, kl, pb, q, s, w, ln, h2, tr_off);
+  else if (DO_PV)
+    gemm_half<DO_PV, false>(vl, kl, pb, q, s, w, ln, h2, tr_off);
+}
+
+template <bool ONLINE>
+__device__ __forceinline__ void softmax_tile(bool full, f32x16 (&s)[2], WaveState& w, bf16x8 (&pb)[4], int lo,
+                                             int hi, int ts, int h2) {
+  if (full)
+    softmax<false, ONLINE>(s, w, pb, lo, hi, ts, h2);
+  else
+    softmax<true, ONLINE>(s, w, pb, lo, hi, ts, h2);
 }
 
 }  // namespace
@@ -193,12 +315,15 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   constexpr int WP = NW * P;   // positions per workgroup
   constexpr int NT = 64 * NW;  // threads per workgroup
   constexpr int LR = 16 / NW;  // K (and V) rows each thread loads per tile
-  // One LDS block, laid out by hand: the double-buffered K and V tiles first
-  // (their addresses stay below 64 KiB, within ds_* immediate offsets), then
-  // each wave's staging rows for its 32 Q rows (prologue) and O rows
-  // (epilogue), so both move between HBM and registers as whole 256-byte rows.
-  constexpr int kTiles = 2 * kTileElemsK + 2 * kTileElemsV;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kTiles + NW * 32 * kLdsStrideK];
+  // One LDS block: K tiles double-buffered, V tiles triple-buffered (tile
+  // t-1's V is still read while tile t+1 is stored).  Each wave's staging
+  // rows for its 32 Q rows (prologue) and O rows (epilogue), through which
+  // both move between HBM and registers as whole 256-byte rows, alias the
+  // tile buffers: they are used only before the first tile is stored and
+  // after the last one is read.
+  constexpr int kTiles = 2 * kTileElemsK + 3 * kTileElemsV;
+  static_assert(NW * 32 * kLdsStrideK <= kTiles, "staging must fit in the tile buffers");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kTiles];
   auto lds_k = [&](int buf) { return lds + buf * kTileElemsK; };
   auto lds_v = [&](int buf) { return lds + 2 * kTileElemsK + buf * kTileElemsV; };
 
@@ -223,7 +348,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
 
   // ---- Q rows of this wave, loaded row-major: 16 lanes x 16 B per row.
   // Staging row x = (head hg, position offset u) is x = hg * P + u.
-  uint16_t* xs = lds + kTiles + wave * 32 * kLdsStrideK;
+  uint16_t* xs = lds + wave * 32 * kLdsStrideK;
   const int x_col = (lane & 15) * 8;
   {
     u32x4 qv[8];
@@ -263,14 +388,25 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   const int ld_row = tid >> 4;
   const uint16_t* khat_head = a.khat + ((long long)b * a.Hkv + g) * a.S * kD + ld_col;
   const uint16_t* v_seq = a.v + ((long long)b * a.S * a.Hkv + g) * kD + ld_col;
-  const long long vstride = (long long)a.Hkv * kD;
+  const int vstride = a.Hkv * kD;
   const long long cache_off = ((long long)b * a.Hkv + g) * (long long)a.cap * kD + ld_col;
-  u32x4 pk[LR], pv[LR];
-  // Branch-free: every lane always loads from a valid address (row 0 of this
-  // head's chunk when its key does not exist) and zeroes the data after, so
-  // all of a tile's 16-byte loads are in flight together.
+  u32x4 pk[LR], pvr[LR];
   bool pvalid[LR];
+  // tile t lies wholly inside this chunk (the common case: no per-row checks)
+  auto chunk_tile = [&](int t) { return t >= 0 && p0 + (t + 1) * kBN <= chunk_end; };
   auto load_tile = [&](int t) {
+    if (chunk_tile(t)) {
+#pragma unroll
+      for (int u = 0; u < LR; ++u) {
+        const int r = t * kBN + ld_row + (NT / 16) * u;
+        pk[u] = *(const u32x4*)(khat_head + r * kD);
+        pvr[u] = *(const u32x4*)(v_seq + r * vstride);
+      }
+      return;
+    }
+    // Edge tiles: every lane still loads from a valid address (row 0 of
+    // this head's chunk when its key does not exist) and the row is zeroed
+    // at the store, so all of a tile's loads stay in flight together.
     const int ts = p0 + t * kBN;
 #pragma unroll
     for (int u = 0; u < LR; ++u) {
@@ -278,25 +414,26 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
       const bool in_chunk = j >= p0 && j < chunk_end;
       const bool in_cache = a.has_cache && j < p0 && j >= kmin_avail;
       const int r = in_chunk ? j - p0 : 0;
-      const uint16_t* kp = khat_head + (long long)r * kD;
-      const uint16_t* vp = v_seq + (long long)r * vstride;
+      const uint16_t* kp = khat_head + r * kD;
+      const uint16_t* vp = v_seq + r * vstride;
       if (in_cache) {
         const long long slot = a.is_ring ? (long long)(j % a.cap) : (long long)j;
         kp = a.ck + cache_off + slot * kD;
         vp = a.cv + cache_off + slot * kD;
       }
       pk[u] = *(const u32x4*)kp;
-      pv[u] = *(const u32x4*)vp;
+      pvr[u] = *(const u32x4*)vp;
       pvalid[u] = in_chunk || in_cache;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int t, int kbuf, int vbuf) {
+    const bool whole = chunk_tile(t);
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < LR; ++u) {
       const int row = ld_row + (NT / 16) * u;
-      *(u32x4*)(lds_k(buf) + row * kLdsStrideK + ld_col) = pvalid[u] ? pk[u] : zero;
-      *(u32x4*)(lds_v(buf) + row * kLdsStrideV + ld_col) = pvalid[u] ? pv[u] : zero;
+      *(u32x4*)(lds_k(kbuf) + row * kLdsStrideK + ld_col) = (whole || pvalid[u]) ? pk[u] : zero;
+      *(u32x4*)(lds_v(vbuf) + row * kLdsStrideV + ld_col) = (whole || pvalid[u]) ? pvr[u] : zero;
     }
   };
 
@@ -362,7 +499,9 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
     }
   }
 
-  store_tile(0);
+  __syncthreads();  // every wave has read its staged Q rows
+  store_tile(t_begin, 0, 0);
+  if (n_t > 1) load_tile(t_begin + 1);
   __syncthreads();
 
   const int tr_g = lane >> 4;
@@ -378,20 +517,80 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
     for (int r = 0; r < 16; ++r) ws.o[mb][r] = 0.f;
   ws.l = 0.f;
   ws.m = -__builtin_huge_valf();
-  for (int it = 0; it < n_t; ++it) {
-    const int t = t_begin + it;
-    const int cur = it & 1;
-    if (it + 1 < n_t) load_tile(t + 1);
-    const int ts = p0 + t * kBN;
-    if (ts <= w_hi_max && ts + kBN - 1 >= w_lo_min) {
-      if (ts >= w_lo_max && ts + kBN - 1 <= w_hi_min)
-        tile_body<false, ONLINE>(lds_k(cur), lds_v(cur), qreg, ws, row_lo, row_hi, ts, ln, h2, tr_off);
-      else
-        tile_body<true, ONLINE>(lds_k(cur), lds_v(cur), qreg, ws, row_lo, row_hi, ts, ln, h2, tr_off);
+  // Ping-pong between the two waves of each SIMD (waves w and w + NW/2):
+  // every tile takes two halves separated by workgroup barriers, and in each
+  // half one wave runs its matrix products (PV of the previous tile, then QK
+  // of this one: 32 MFMAs) while the other runs its softmax (VALU), so the
+  // MFMA pipe and the VALU are busy at the same time instead of in turn.
+  //   group A (waves 0..NW/2-1): half 1 PV(t-1) + QK(t), half 2 softmax(t)
+  //   group B (waves NW/2..NW-1): half 1 softmax(t-1),   half 2 PV(t-1) + QK(t)
+  auto run = [&](auto grp_b_tag) {
+    constexpr bool GB = decltype(grp_b_tag)::value;
+    f32x16 s[2];
+    bf16x8 pb[4];
+    bool have_p = false;  // pb holds p of the previous tile, PV still to do
+    bool have_s = false;  // (group B) s holds scores of the previous tile
+    bool s_full = false;
+    int s_ts = 0;
+    int vprev = 2;  // V buffer of tile t-1
+    for (int it = 0; it < n_t; ++it) {
+      const int t = t_begin + it;
+      const int kcur = it & 1;
+      const int vcur = vprev == 2 ? 0 : vprev + 1;
+      const int vnext = vcur == 2 ? 0 : vcur + 1;
+      const int ts = p0 + t * kBN;
+      const bool act = ts <= w_hi_max && ts + kBN - 1 >= w_lo_min;
+      const bool full = ts >= w_lo_max && ts + kBN - 1 <= w_hi_min;
+      // tile t+1 (loaded during the previous tile) goes to LDS, tile t+2's
+      // loads are issued: VALU-side work, done in the softmax half
+      auto stage_tiles = [&]() {
+        if (it + 1 < n_t) store_tile(t + 1, kcur ^ 1, vnext);
+        if (it + 2 < n_t) load_tile(t + 2);
+      };
+      if (!GB) {
+        if (have_p)
+          gemm_step<true>(act, lds_v(vprev), lds_k(kcur), pb, qreg, s, ws, ln, h2, tr_off);
+        else
+          gemm_step<false>(act, lds_v(vprev), lds_k(kcur), pb, qreg, s, ws, ln, h2, tr_off);
+        have_p = false;
+        __syncthreads();
+        if (act) {
+          softmax_tile<ONLINE>(full, s, ws, pb, row_lo, row_hi, ts, h2);
+          have_p = true;
+        }
+        stage_tiles();
+        __syncthreads();
+      } else {
+        if (have_s) {
+          softmax_tile<ONLINE>(s_full, s, ws, pb, row_lo, row_hi, s_ts, h2);
+          have_p = true;
+        }
+        stage_tiles();
+        __syncthreads();
+        if (have_p)
+          gemm_step<true>(act, lds_v(vprev), lds_k(kcur), pb, qreg, s, ws, ln, h2, tr_off);
+        else
+          gemm_step<false>(act, lds_v(vprev), lds_k(kcur), pb, qreg, s, ws, ln, h2, tr_off);
+        have_p = false;
+        have_s = act;
+        s_full = full;
+        s_ts = ts;
+        __syncthreads();
+      }
+      vprev = vcur;
     }
-    if (it + 1 < n_t) store_tile(cur ^ 1);
+    // drain: the last tile's PV (group A) / softmax then PV (group B)
+    if (GB && have_s) {
+      softmax_tile<ONLINE>(s_full, s, ws, pb, row_lo, row_hi, s_ts, h2);
+      have_p = true;
+    }
     __syncthreads();
-  }
+    if (have_p) pv(lds_v(vprev), pb, ws, tr_off);
+  };
+  if (__builtin_amdgcn_readfirstlane(tid >> 6) >= NW / 2)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // Fast pass (ONLINE = false): QK-RMSNorm bounds every logit by
   // scale * D * max|gamma_q| * max|gamma_k|, so for sane gammas the softmax
@@ -402,9 +601,11 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   const float lt = xhalf_sum(ws.l);
   if (!ONLINE) {
     const bool bad = row_ok && !(lt >= 0x1p-64f && lt <= 0x1p64f);
-    const int any_bad = __syncthreads_or(bad);
+    const int any_bad = __syncthreads_or(bad);  // also: every wave is past its last V read
     if (tid == 0) a.flags[li] = any_bad;
     if (any_bad) return;
+  } else {
+    __syncthreads();  // every wave is past its last V read
   }
 
   // ---- epilogue: O / l to bf16 into the wave's staging rows, then whole

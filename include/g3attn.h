@@ -103,7 +103,9 @@ int g3attn_qknorm_rope(const g3_bf16* q_in, const g3_bf16* k_in, g3_bf16* q_out,
  *   are written to their slots (a ring keeps only its last `capacity`).
  *   A linear cache needs capacity >= pos0[b] + S.
  * workspace: device, >= g3attn_prefill_workspace_size(B, S, Hq, Hkv, D)
- *   bytes, 256-byte aligned; its contents on entry do not matter. */
+ *   bytes, 256-byte aligned; its contents on entry do not matter.
+ * Limits: B*S*Hq < 2^31 (else G3_EINVAL) and S*Hkv*D < 2^31 (element
+ *   offsets inside one sequence are 32-bit; else G3_EUNSUPPORTED). */
 int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16* o,
                    int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
                    int32_t layer_kind, int32_t window, float rope_base, float interp_scale,

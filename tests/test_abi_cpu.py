@@ -72,6 +72,8 @@ def test_prefill_validation_errors(L):
     assert _prefill(L, q=FAKE + 2) == G.G3_EINVAL and "aligned" in _err(L)
     assert _prefill(L, ws_bytes=10) == G.G3_EWORKSPACE
     assert _prefill(L, ws=FAKE + 16) == G.G3_EINVAL
+    # per-sequence element offsets are 32-bit: S * Hkv * D must stay below 2^31
+    assert _prefill(L, S=1 << 20, Hq=16, Hkv=16) == G.G3_EUNSUPPORTED and "32-bit" in _err(L)
     sp = (G.Span * 2)(G.Span(0, 10, 20), G.Span(0, 15, 30))
     assert _prefill(L, spans=sp, n_spans=2) == G.G3_EINVAL and "overlapping" in _err(L)
     sp = (G.Span * 1)(G.Span(0, 60, 70))
