@@ -36,18 +36,23 @@ namespace g3 {
 
 namespace {
 
-constexpr int kBN = 64;           // keys per LDS tile (two halves of 32)
-// LDS row strides (bf16 elements), chosen by measured read rate on gfx950
-// (64 banks of 4 bytes).  K rows are read 16 B per lane by 32 lanes of
-// different rows (S^T A operand): 256 + 16 B per row runs at the full LDS
-// rate.  V rows are read by ds_read_b64_tr_b16, each 16-lane group covering
-// 4 rows x 32 B and two groups 4 rows x 64 B: 256 + 64 B per row puts the
-// rows a 32-lane half touches on disjoint banks (256 + 32 B conflicts 2-way
-// on half of them).
-constexpr int kLdsStrideK = 136;
-constexpr int kLdsStrideV = 160;
-constexpr int kTileElemsK = kBN * kLdsStrideK;
-constexpr int kTileElemsV = kBN * kLdsStrideV;
+constexpr int kBN = 64;  // keys per LDS tile (two halves of 32)
+// K and V tiles sit in LDS as 64 rows x 256 B with no padding; the 16-byte
+// chunk c of row r is stored at chunk position c ^ swz(r).  The swizzle makes
+// both operand reads conflict-free on gfx950's 64 x 4-byte banks: the K read
+// (32 lanes on 32 rows, one chunk each) and the transposing V read (groups
+// of 16 lanes on 4 rows x 32 B).  Tiles are filled by global->LDS loads that
+// write 64 consecutive 16-byte chunks per instruction, so the swizzle is
+// applied by choosing which chunk each lane fetches.
+constexpr int kTileElems = kBN * 128;  // bf16 elements per tile
+constexpr int kStageStride = 136;      // Q/O staging rows: 256 + 16 B
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// Per-lane byte offsets of the operand reads inside a tile.
+struct TileAddr {
+  uint32_t k[8];     // K^T operand, dims step st (key half kb adds 32 rows = 8192 B)
+  uint32_t v[2][4];  // V^T operand, [row half][dim block] (key step t adds 16 rows = 4096 B)
+};
 
 __device__ __forceinline__ int wave_min_i(int x) {
 #pragma unroll
@@ -77,6 +82,44 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// Workgroup barrier that waits only for this wave's LDS operations: tile
+// loads still in flight from global memory into LDS keep flying (a
+// __syncthreads() would wait for every outstanding memory operation).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// All but this wave's `newer` most recent global->LDS tile loads (0 or 4)
+// have landed; loads complete in issue order.
+__device__ __forceinline__ void wait_tile_loads_but(int newer) {
+  if (newer == 4)
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// One 16-byte global -> LDS load per lane (global_load_lds_dwordx4): lane L
+// writes LDS bytes [lds_addr + 16 L, +16), lds_addr taken from M0.  Written
+// as inline asm rather than the builtin so the compiler does not treat every
+// later LDS read as dependent on it (it cannot tell the tile buffers apart
+// and would wait for all loads in flight); the kernel orders these loads
+// itself with wait_tile_loads_but() before the barrier that publishes a tile.
+// M0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_addr));
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)p);
+}
+
+// A zero K/V row: the source of tile rows whose key does not exist.
+__device__ __attribute__((aligned(256))) uint16_t g_zero_row[128] = {0};
 
 __device__ __forceinline__ int floor_div64(int x) { return x >= 0 ? x / 64 : -((63 - x) / 64); }
 
@@ -112,20 +155,6 @@ struct WaveState {
 //            row sums, p packed to bf16 as the B operand of P V
 //   pv:      O^T (128 dims x 32 queries) += V^T P^T, 16 MFMA, V^T through
 //            transposing LDS reads
-__device__ __forceinline__ void qk(const uint16_t* kl, const bf16x8 (&q)[8], f32x16 (&s)[2], int ln, int h2) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-  for (int st = 0; st < 8; ++st)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 kop = *(const bf16x8*)(kl + (kb * 32 + ln) * kLdsStrideK + 16 * st + 8 * h2);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[st], s[kb], 0, 0, 0);
-    }
-}
-
 template <bool MASK, bool ONLINE>
 __device__ __forceinline__ void softmax(f32x16 (&s)[2], WaveState& w, bf16x8 (&pb)[4], int lo, int hi, int ts,
                                         int h2) {
@@ -174,26 +203,11 @@ __device__ __forceinline__ void softmax(f32x16 (&s)[2], WaveState& w, bf16x8 (&p
   w.l += rs;
 }
 
-__device__ __forceinline__ void pv(const uint16_t* vl, const bf16x8 (&pb)[4], WaveState& w, int tr_off) {
-  // V^T operands of 16-key step t are read one step ahead of their MFMAs
-  bf16x8 vop[2][4];
-  auto read_step = [&](int t, bf16x8 (&dst)[4]) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const uint16_t* base = vl + 16 * t * kLdsStrideV + 32 * mb + tr_off;
-      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
-      const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * kLdsStrideV));
-      dst[mb] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  };
-  read_step(0, vop[0]);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (t < 3) read_step(t + 1, vop[(t + 1) & 1]);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      w.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t & 1][mb], pb[t], w.o[mb], 0, 0, 0);
-  }
+__device__ __forceinline__ bf16x8 read_v(const uint16_t* vl, const TileAddr& ad, int t, int mb) {
+  const char* base = (const char*)vl + 4096 * t;
+  const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + ad.v[0][mb]));
+  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + ad.v[1][mb]));
+  return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // The matrix half of a tile step: PV of the previous tile (if DO_PV) then QK
@@ -201,25 +215,26 @@ __device__ __forceinline__ void pv(const uint16_t* vl, const bf16x8 (&pb)[4], Wa
 // (256 MFMA cycles) or four QK steps ahead of the MFMAs that use them, and
 // scheduling fences keep the compiler from pulling them back next to their
 // uses, where each MFMA would wait out a full LDS latency.
-template <bool DO_PV, bool DO_QK>
-__device__ __forceinline__ void gemm_half(const uint16_t* vl, const uint16_t* kl, const bf16x8 (&pb)[4],
-                                          const bf16x8 (&q)[8], f32x16 (&s)[2], WaveState& w, int ln, int h2,
-                                          int tr_off) {
+// The matrix half of a tile step: PV of the previous tile (if DO_PV) then QK
+// of this one (if DO_QK), 16 + 16 MFMAs.  LDS operand reads run two PV steps
+// (256 MFMA cycles) or four QK steps ahead of the MFMAs that use them, and
+// scheduling fences keep the compiler from pulling them back next to their
+// uses, where each MFMA would wait out a full LDS latency.  dma(k), k = 0..7,
+// issues the wave's share of the next tile's global->LDS loads, spread
+// between the MFMA groups so each waits for the memory pipeline on its own.
+template <bool DO_PV, bool DO_QK, typename Dma>
+__device__ __forceinline__ void gemm_half(const uint16_t* vl, const uint16_t* kl, const TileAddr& ad,
+                                          const bf16x8 (&pb)[4], const bf16x8 (&q)[8], f32x16 (&s)[2],
+                                          WaveState& w, Dma&& dma) {
   bf16x8 vop[4][4];  // [16-key step][dim block]
   bf16x8 kop[8][2];  // [16-dim step][key half]
   auto rd_v = [&](int t) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const uint16_t* base = vl + 16 * t * kLdsStrideV + 32 * mb + tr_off;
-      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
-      const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * kLdsStrideV));
-      vop[t][mb] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
+    for (int mb = 0; mb < 4; ++mb) vop[t][mb] = read_v(vl, ad, t, mb);
   };
   auto rd_k = [&](int st) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      kop[st][kb] = *(const bf16x8*)(kl + (kb * 32 + ln) * kLdsStrideK + 16 * st + 8 * h2);
+    for (int kb = 0; kb < 2; ++kb) kop[st][kb] = *(const bf16x8*)((const char*)kl + ad.k[st] + 8192 * kb);
   };
   auto mm_pv = [&](int t) {
 #pragma unroll
@@ -250,21 +265,25 @@ __device__ __forceinline__ void gemm_half(const uint16_t* vl, const uint16_t* kl
   if (DO_PV) {
     mm_pv(0);
     rd_v(2);
+    dma(0);
     fence();
     mm_pv(1);
     rd_v(3);
+    dma(1);
     fence();
     mm_pv(2);
     if (DO_QK) {
       rd_k(2);
       rd_k(3);
     }
+    dma(2);
     fence();
     mm_pv(3);
     if (DO_QK) {
       rd_k(4);
       rd_k(5);
     }
+    dma(3);
     fence();
   } else if (DO_QK) {
     rd_k(2);
@@ -276,19 +295,32 @@ __device__ __forceinline__ void gemm_half(const uint16_t* vl, const uint16_t* kl
     for (int st = 0; st < 8; ++st) {
       mm_qk(st);
       if (st + KA < 8) rd_k(st + KA);
+      if (DO_PV) {
+        if (st & 1) dma(4 + (st >> 1));
+      } else {
+        dma(st);
+      }
       fence();
     }
   }
+  if (DO_PV && !DO_QK) {
+#pragma unroll
+    for (int k = 4; k < 8; ++k) dma(k);
+  }
 }
 
-template <bool DO_PV>
-__device__ __forceinline__ void gemm_step(bool do_qk, const uint16_t* vl, const uint16_t* kl, const bf16x8 (&pb)[4],
-                                          const bf16x8 (&q)[8], f32x16 (&s)[2], WaveState& w, int ln, int h2,
-                                          int tr_off) {
-  if (do_qk)
-    gemm_half<DO_PV, true>(vl, kl, pb, q, s, w, ln, h2, tr_off);
-  else if (DO_PV)
-    gemm_half<DO_PV, false>(vl, kl, pb, q, s, w, ln, h2, tr_off);
+template <bool DO_PV, typename Dma>
+__device__ __forceinline__ void gemm_step(bool do_qk, const uint16_t* vl, const uint16_t* kl, const TileAddr& ad,
+                                          const bf16x8 (&pb)[4], const bf16x8 (&q)[8], f32x16 (&s)[2],
+                                          WaveState& w, Dma&& dma) {
+  if (do_qk) {
+    gemm_half<DO_PV, true>(vl, kl, ad, pb, q, s, w, dma);
+  } else if (DO_PV) {
+    gemm_half<DO_PV, false>(vl, kl, ad, pb, q, s, w, dma);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dma(k);
+  }
 }
 
 template <bool ONLINE>
@@ -314,18 +346,18 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   constexpr int P = 32 / G;    // positions per wave
   constexpr int WP = NW * P;   // positions per workgroup
   constexpr int NT = 64 * NW;  // threads per workgroup
-  constexpr int LR = 16 / NW;  // K (and V) rows each thread loads per tile
-  // One LDS block: K tiles double-buffered, V tiles triple-buffered (tile
-  // t-1's V is still read while tile t+1 is stored).  Each wave's staging
-  // rows for its 32 Q rows (prologue) and O rows (epilogue), through which
-  // both move between HBM and registers as whole 256-byte rows, alias the
-  // tile buffers: they are used only before the first tile is stored and
-  // after the last one is read.
-  constexpr int kTiles = 2 * kTileElemsK + 3 * kTileElemsV;
-  static_assert(NW * 32 * kLdsStrideK <= kTiles, "staging must fit in the tile buffers");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kTiles];
-  auto lds_k = [&](int buf) { return lds + buf * kTileElemsK; };
-  auto lds_v = [&](int buf) { return lds + 2 * kTileElemsK + buf * kTileElemsV; };
+  static_assert(NW == 8, "the tile loader gives each wave 8 of the 64 rows");
+  // LDS, 16 KiB per tile buffer: K in 3 buffers and V in 4 (tile t is read,
+  // tile t+1 has landed or is landing, tile t+2 is being fetched; V of tile
+  // t-1 is still read by the PV half).  Order: K0 V0 K1 K2 V1 V2 V3.  Each
+  // wave's staging rows for its 32 Q rows (prologue) and O rows (epilogue),
+  // through which both move between HBM and registers as whole 256-byte rows,
+  // alias K1..V3: the first tile (K0, V0) lands while Q is staged, and the
+  // second is only fetched once every wave has read its Q rows.
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[7 * kTileElems];
+  static_assert(NW * 32 * kStageStride <= 5 * kTileElems, "staging must fit in K1..V3");
+  auto lds_k = [&](int buf) { return lds + (buf == 0 ? 0 : buf + 1) * kTileElems; };
+  auto lds_v = [&](int buf) { return lds + (buf == 0 ? 1 : buf + 3) * kTileElems; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -348,7 +380,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
 
   // ---- Q rows of this wave, loaded row-major: 16 lanes x 16 B per row.
   // Staging row x = (head hg, position offset u) is x = hg * P + u.
-  uint16_t* xs = lds + wave * 32 * kLdsStrideK;
+  uint16_t* xs = lds + 2 * kTileElems + wave * 32 * kStageStride;
   const int x_col = (lane & 15) * 8;
   {
     u32x4 qv[8];
@@ -361,7 +393,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
       qv[k] = *(const u32x4*)(a.q + (((long long)b * a.S + r) * a.Hq + g * G + hg) * kD + x_col);
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) *(u32x4*)(xs + (4 * k + (lane >> 4)) * kLdsStrideK + x_col) = qv[k];
+    for (int k = 0; k < 8; ++k) *(u32x4*)(xs + (4 * k + (lane >> 4)) * kStageStride + x_col) = qv[k];
   }
 
   // ---- key ranges.  lo(i) and hi(i) are non-decreasing in i, so the union
@@ -383,61 +415,77 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
     w_hi_max = l.hi;
   }
 
-  // ---- tile loader: 16 threads per 256-byte row, LR rows per thread
-  const int ld_col = (tid & 15) * 8;
-  const int ld_row = tid >> 4;
-  const uint16_t* khat_head = a.khat + ((long long)b * a.Hkv + g) * a.S * kD + ld_col;
-  const uint16_t* v_seq = a.v + ((long long)b * a.S * a.Hkv + g) * kD + ld_col;
+  // ---- tile loader: global -> LDS directly (no registers, no LDS stores).
+  // Wave w fills rows [8w, 8w + 8) of the K and V tiles with 4-row
+  // instructions: lane L of instruction i lands on row 8w + 4i + L/16, chunk
+  // position L % 16, so it fetches logical chunk (L % 16) ^ swz(row).  Keys
+  // that do not exist read a zero row, so their p v terms vanish.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int dma_r = lane >> 4;
+  const uint16_t* khat_bg = a.khat + ((long long)b * a.Hkv + g) * a.S * kD;
+  const uint16_t* v_bg = a.v + ((long long)b * a.S * a.Hkv + g) * kD;
   const int vstride = a.Hkv * kD;
-  const long long cache_off = ((long long)b * a.Hkv + g) * (long long)a.cap * kD + ld_col;
-  u32x4 pk[LR], pvr[LR];
-  bool pvalid[LR];
-  // tile t lies wholly inside this chunk (the common case: no per-row checks)
-  auto chunk_tile = [&](int t) { return t >= 0 && p0 + (t + 1) * kBN <= chunk_end; };
-  auto load_tile = [&](int t) {
-    if (chunk_tile(t)) {
-#pragma unroll
-      for (int u = 0; u < LR; ++u) {
-        const int r = t * kBN + ld_row + (NT / 16) * u;
-        pk[u] = *(const u32x4*)(khat_head + r * kD);
-        pvr[u] = *(const u32x4*)(v_seq + r * vstride);
-      }
-      return;
-    }
-    // Edge tiles: every lane still loads from a valid address (row 0 of
-    // this head's chunk when its key does not exist) and the row is zeroed
-    // at the store, so all of a tile's loads stay in flight together.
+  const long long cache_bg = ((long long)b * a.Hkv + g) * (long long)a.cap * kD;
+  const uint16_t* ck_bg = a.has_cache ? a.ck + cache_bg : nullptr;
+  const uint16_t* cv_bg = a.has_cache ? a.cv + cache_bg : nullptr;
+  // Instruction k (0..3) of this wave's share of tile t (k < 2: K rows, else
+  // V rows).  Tiles wholly inside the chunk or wholly inside the cache (the
+  // long-context case) take cheap uniform paths; only boundary tiles check
+  // every row.
+  auto dma_tile = [&](int t, int kbuf, int vbuf) {
     const int ts = p0 + t * kBN;
+    const int mode = (t >= 0 && ts + kBN <= chunk_end) ? 0
+                     : (a.has_cache && ts >= kmin_avail && ts + kBN <= p0 && (!a.is_ring || a.cap >= kBN)) ? 1
+                                                                                                  : 2;
+    // ring slot of the tile's first key (a ring of >= 64 slots wraps at most
+    // once inside a tile)
+    const int slot0 = (mode == 1 && a.is_ring) ? ts % a.cap : ts;
 #pragma unroll
-    for (int u = 0; u < LR; ++u) {
-      const int j = ts + ld_row + (NT / 16) * u;
-      const bool in_chunk = j >= p0 && j < chunk_end;
-      const bool in_cache = a.has_cache && j < p0 && j >= kmin_avail;
-      const int r = in_chunk ? j - p0 : 0;
-      const uint16_t* kp = khat_head + r * kD;
-      const uint16_t* vp = v_seq + r * vstride;
-      if (in_cache) {
-        const long long slot = a.is_ring ? (long long)(j % a.cap) : (long long)j;
-        kp = a.ck + cache_off + slot * kD;
-        vp = a.cv + cache_off + slot * kD;
+    for (int k = 0; k < 4; ++k) {
+      const int i = k & 1;
+      const bool is_v = k >= 2;
+      const int col = ((lane & 15) ^ ((dma_r << 2) | ((2 * wave + i) & 3))) * 8;
+      const int row = 8 * wave + 4 * i + dma_r;
+      const uint16_t* src;
+      if (mode == 0) {
+        const int r = t * kBN + row;
+        src = is_v ? v_bg + r * vstride : khat_bg + r * kD;
+      } else if (mode == 1) {
+        int slot = slot0 + row;
+        if (a.is_ring && slot >= a.cap) slot -= a.cap;
+        src = (is_v ? cv_bg : ck_bg) + (long long)slot * kD;
+      } else {
+        const int j = ts + row;
+        src = g_zero_row;
+        if (j >= p0 && j < chunk_end) {
+          src = is_v ? v_bg + (j - p0) * vstride : khat_bg + (j - p0) * kD;
+        } else if (a.has_cache && j < p0 && j >= kmin_avail) {
+          const long long slot = a.is_ring ? (long long)(j % a.cap) : (long long)j;
+          src = (is_v ? cv_bg : ck_bg) + slot * kD;
+        }
       }
-      pk[u] = *(const u32x4*)kp;
-      pvr[u] = *(const u32x4*)vp;
-      pvalid[u] = in_chunk || in_cache;
-    }
-  };
-  auto store_tile = [&](int t, int kbuf, int vbuf) {
-    const bool whole = chunk_tile(t);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int u = 0; u < LR; ++u) {
-      const int row = ld_row + (NT / 16) * u;
-      *(u32x4*)(lds_k(kbuf) + row * kLdsStrideK + ld_col) = (whole || pvalid[u]) ? pk[u] : zero;
-      *(u32x4*)(lds_v(vbuf) + row * kLdsStrideV + ld_col) = (whole || pvalid[u]) ? pvr[u] : zero;
+      const uint16_t* dst = (is_v ? lds_v(vbuf) : lds_k(kbuf)) + (8 * wave_u + 4 * i) * kD;
+      dma16(src + col, lds_addr_of(dst));
     }
   };
 
-  load_tile(t_begin);  // in flight while Q is prepared
+  // operand read offsets inside a tile (see TileAddr)
+  TileAddr ad;
+#pragma unroll
+  for (int st = 0; st < 8; ++st) ad.k[st] = ln * 256 + ((((2 * st + h2) ^ swz(ln))) << 4);
+  {
+    const int g4 = lane >> 4, w16 = lane & 15;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int row = 8 * hf + 4 * (g4 >> 1) + (w16 >> 2);
+        const int c = 4 * mb + 2 * (g4 & 1) + ((w16 & 3) >> 1);
+        ad.v[hf][mb] = row * 256 + ((c ^ swz(row)) << 4) + 8 * (w16 & 1);
+      }
+  }
+
+  dma_tile(t_begin, 0, 0);  // the first tile, in flight while Q is prepared
 
   // this lane's query row: position offset ln % P, head ln / P of the group
   const int hg = ln / P;
@@ -460,7 +508,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
     float x[64];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const u32x4 wv = *(const u32x4*)(xs + ln * kLdsStrideK + 16 * s + 8 * h2);
+      const u32x4 wv = *(const u32x4*)(xs + ln * kStageStride + 16 * s + 8 * h2);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         x[8 * s + 2 * e] = bf_lo(wv[e]);
@@ -499,16 +547,10 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
     }
   }
 
-  __syncthreads();  // every wave has read its staged Q rows
-  store_tile(t_begin, 0, 0);
-  if (n_t > 1) load_tile(t_begin + 1);
-  __syncthreads();
-
-  const int tr_g = lane >> 4;
-  const int tr_w = lane & 15;
-  // transposing-read offset (ds_read_b64_tr_b16 works on groups of 16 lanes):
-  // key row 4*(group/2) + w/4 (+ 16 t + 8 r), dims 16*(group&1) + 4*(w&3) (+ 32 mb)
-  const int tr_off = (4 * (tr_g >> 1) + (tr_w >> 2)) * kLdsStrideV + 16 * (tr_g & 1) + 4 * (tr_w & 3);
+  barrier_lds();  // every wave has read its staged Q rows
+  if (n_t > 1) dma_tile(t_begin + 1, 1, 1);
+  wait_tile_loads_but(n_t > 1 ? 4 : 0);
+  barrier_lds();  // the first tile is in LDS
 
   WaveState ws;
 #pragma unroll
@@ -532,60 +574,67 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
     bool have_s = false;  // (group B) s holds scores of the previous tile
     bool s_full = false;
     int s_ts = 0;
-    int vprev = 2;  // V buffer of tile t-1
     for (int it = 0; it < n_t; ++it) {
       const int t = t_begin + it;
-      const int kcur = it & 1;
-      const int vcur = vprev == 2 ? 0 : vprev + 1;
-      const int vnext = vcur == 2 ? 0 : vcur + 1;
+      const int kcur = it % 3;
+      const int vcur = it & 3;
+      const int vprev = (it + 3) & 3;
       const int ts = p0 + t * kBN;
       const bool act = ts <= w_hi_max && ts + kBN - 1 >= w_lo_min;
       const bool full = ts >= w_lo_max && ts + kBN - 1 <= w_hi_min;
-      // tile t+1 (loaded during the previous tile) goes to LDS, tile t+2's
-      // loads are issued: VALU-side work, done in the softmax half
-      auto stage_tiles = [&]() {
-        if (it + 1 < n_t) store_tile(t + 1, kcur ^ 1, vnext);
-        if (it + 2 < n_t) load_tile(t + 2);
+      // Tile t+2 is fetched during this wave's softmax half (VALU-bound, with
+      // slack next to the other wave's matrix half); before the tile's closing
+      // barrier only tile t+1's loads must have landed.
+      const bool fetch = it + 2 < n_t;
+      auto prefetch = [&]() {
+        if (fetch) dma_tile(t + 2, (it + 2) % 3, (it + 2) & 3);
       };
+      auto no_dma = [](int) {};
       if (!GB) {
+        __builtin_amdgcn_s_setprio(1);
         if (have_p)
-          gemm_step<true>(act, lds_v(vprev), lds_k(kcur), pb, qreg, s, ws, ln, h2, tr_off);
+          gemm_step<true>(act, lds_v(vprev), lds_k(kcur), ad, pb, qreg, s, ws, no_dma);
         else
-          gemm_step<false>(act, lds_v(vprev), lds_k(kcur), pb, qreg, s, ws, ln, h2, tr_off);
+          gemm_step<false>(act, lds_v(vprev), lds_k(kcur), ad, pb, qreg, s, ws, no_dma);
+        __builtin_amdgcn_s_setprio(0);
         have_p = false;
-        __syncthreads();
+        barrier_lds();
         if (act) {
           softmax_tile<ONLINE>(full, s, ws, pb, row_lo, row_hi, ts, h2);
           have_p = true;
         }
-        stage_tiles();
-        __syncthreads();
+        prefetch();
+        wait_tile_loads_but(fetch ? 4 : 0);
+        barrier_lds();
       } else {
         if (have_s) {
           softmax_tile<ONLINE>(s_full, s, ws, pb, row_lo, row_hi, s_ts, h2);
           have_p = true;
         }
-        stage_tiles();
-        __syncthreads();
+        prefetch();
+        barrier_lds();
+        __builtin_amdgcn_s_setprio(1);
         if (have_p)
-          gemm_step<true>(act, lds_v(vprev), lds_k(kcur), pb, qreg, s, ws, ln, h2, tr_off);
+          gemm_step<true>(act, lds_v(vprev), lds_k(kcur), ad, pb, qreg, s, ws, no_dma);
         else
-          gemm_step<false>(act, lds_v(vprev), lds_k(kcur), pb, qreg, s, ws, ln, h2, tr_off);
+          gemm_step<false>(act, lds_v(vprev), lds_k(kcur), ad, pb, qreg, s, ws, no_dma);
+        __builtin_amdgcn_s_setprio(0);
         have_p = false;
         have_s = act;
         s_full = full;
         s_ts = ts;
-        __syncthreads();
+        wait_tile_loads_but(fetch ? 4 : 0);
+        barrier_lds();
       }
-      vprev = vcur;
     }
+    const int vprev = (n_t + 3) & 3;  // V buffer of the last tile
     // drain: the last tile's PV (group A) / softmax then PV (group B)
     if (GB && have_s) {
       softmax_tile<ONLINE>(s_full, s, ws, pb, row_lo, row_hi, s_ts, h2);
       have_p = true;
     }
-    __syncthreads();
-    if (have_p) pv(lds_v(vprev), pb, ws, tr_off);
+    barrier_lds();
+    if (have_p) gemm_half<true, false>(lds_v(vprev), lds_k(0), ad, pb, qreg, s, ws, [](int) {});
   };
   if (__builtin_amdgcn_readfirstlane(tid >> 6) >= NW / 2)
     run(std::true_type{});
@@ -605,7 +654,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
     if (tid == 0) a.flags[li] = any_bad;
     if (any_bad) return;
   } else {
-    __syncthreads();  // every wave is past its last V read
+    barrier_lds();  // every wave is past its last V read (staging aliases the tiles)
   }
 
   // ---- epilogue: O / l to bf16 into the wave's staging rows, then whole
@@ -618,7 +667,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * mb + 8 * q4 + 4 * h2;
         const f32x16& oa = ws.o[mb];
-        *(u32x2*)(xs + ln * kLdsStrideK + d) = u32x2{pack2(oa[4 * q4] * inv, oa[4 * q4 + 1] * inv),
+        *(u32x2*)(xs + ln * kStageStride + d) = u32x2{pack2(oa[4 * q4] * inv, oa[4 * q4 + 1] * inv),
                                                      pack2(oa[4 * q4 + 2] * inv, oa[4 * q4 + 3] * inv)};
       }
   }
@@ -633,7 +682,7 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   for (int k = 0; k < 8; ++k) {
     const int x = 4 * k + (el >> 4);
     const int xh = x / P, u = x - (x / P) * P;
-    const u32x4 ov = *(const u32x4*)(xs + x * kLdsStrideK + e_col);
+    const u32x4 ov = *(const u32x4*)(xs + x * kStageStride + e_col);
     if (wbase + u < chunk_end) *(u32x4*)(o_wave + (u * a.Hq + xh) * kD + e_col) = ov;
   }
 }
