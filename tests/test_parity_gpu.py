@@ -195,19 +195,25 @@ def _fill_cache_host(k_raw, v_raw, gk, cap, is_ring, base, scale, n):
     return ck, cv
 
 
-@pytest.mark.parametrize("kind,is_ring,cap", [(A.GLOBAL, False, 3000), (A.LOCAL, True, 1024), (A.LOCAL, False, 3000)])
-def test_chunked_prefill_against_cache(kind, is_ring, cap):
+# p0 = 1500 puts the cache/chunk boundary inside a key tile; p0 = 1536 on a tile edge (every cache tile
+# whole).  The 48-slot ring (window 40) is smaller than a key tile, so its slots repeat inside one tile.
+@pytest.mark.parametrize("kind,is_ring,cap,p0,window", [(A.GLOBAL, False, 3000, 1500, W.WINDOW),
+                                                        (A.LOCAL, True, 1024, 1500, W.WINDOW),
+                                                        (A.LOCAL, False, 3000, 1500, W.WINDOW),
+                                                        (A.GLOBAL, False, 3000, 1536, W.WINDOW),
+                                                        (A.LOCAL, True, 1024, 1536, W.WINDOW),
+                                                        (A.LOCAL, True, 48, 1536, 40)])
+def test_chunked_prefill_against_cache(kind, is_ring, cap, p0, window):
     B, Stot, Hq, Hkv = 1, 2600, 4, 2
     q, k, v, gq, gk = _inputs(4, kind, B, Stot, Hq, Hkv)
     base, scale = _kind_params(kind, 8.0)
-    p0 = 1500
     ck, cv = _fill_cache_host(k, v, gk, cap, is_ring, base, scale, p0)
     cache = G.KVCache(dev_bf16(ck), dev_bf16(cv), is_ring)
     spans = [[(1600, 1856)]]
-    o = G.prefill(dev_bf16(q[:, p0:]), dev_bf16(k[:, p0:]), dev_bf16(v[:, p0:]), kind, W.WINDOW, base, scale,
+    o = G.prefill(dev_bf16(q[:, p0:]), dev_bf16(k[:, p0:]), dev_bf16(v[:, p0:]), kind, window, base, scale,
                   dev_f32(gq), dev_f32(gk), W.EPS, 0.0, [(0, 1600, 1856)], [p0], cache)
     torch.cuda.synchronize()
-    ref, rck, rcv = A.prefill_chunk(q[:, p0:], k[:, p0:], v[:, p0:], ck, cv, is_ring, kind, W.WINDOW, base, scale,
+    ref, rck, rcv = A.prefill_chunk(q[:, p0:], k[:, p0:], v[:, p0:], ck, cv, is_ring, kind, window, base, scale,
                                     gq, gk, W.EPS, spans=spans, pos0=[p0])
     assert_parity(host(o), ref, f"chunk kind={kind} ring={is_ring}")
     assert np.array_equal(host(cache.v), rcv)
