@@ -340,9 +340,10 @@ __device__ __forceinline__ void softmax_tile(bool full, f32x16 (&s)[2], WaveStat
 // one workgroup fills a CU (two waves per SIMD): one wave's softmax VALU
 // work overlaps the other's MFMAs, and each K/V tile crosses L2 -> LDS once
 // per 256 query rows.
+// One work item: (sequence, kv head, query tile) li.
 template <int G, bool ONLINE, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW)
-void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt,
+                                             const RopeTable& rt, uint16_t* lds, int li) {
   constexpr int P = 32 / G;    // positions per wave
   constexpr int WP = NW * P;   // positions per workgroup
   constexpr int NT = 64 * NW;  // threads per workgroup
@@ -354,7 +355,6 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   // through which both move between HBM and registers as whole 256-byte rows,
   // alias K1..V3: the first tile (K0, V0) lands while Q is staged, and the
   // second is only fetched once every wave has read its Q rows.
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[7 * kTileElems];
   static_assert(NW * 32 * kStageStride <= 5 * kTileElems, "staging must fit in K1..V3");
   auto lds_k = [&](int buf) { return lds + (buf == 0 ? 0 : buf + 1) * kTileElems; };
   auto lds_v = [&](int buf) { return lds + (buf == 0 ? 1 : buf + 3) * kTileElems; };
@@ -365,7 +365,6 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   const int h2 = lane >> 5;
   const int ln = lane & 31;
 
-  const int li = xcd_remap(blockIdx.x, gridDim.x);
   // The online-maximum pass only redoes the tiles the fast pass flagged.
   if (ONLINE && a.flags[li] == 0) return;
   const int bg = li / a.n_qtiles;
@@ -687,9 +686,43 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   }
 }
 
+// Workgroup g takes items xcd_remap(g) + k * gridDim.x: with fewer
+// workgroups than items (the local layers, whose items all cost the same)
+// each workgroup runs several items back to back on its CU, and the
+// workgroups of one XCD always work on neighbouring query tiles of the same
+// kv head, which share K/V in that XCD's L2.
+template <int G, bool ONLINE, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW)
+void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[7 * kTileElems];
+  const int n_items = a.B * a.Hkv * a.n_qtiles;
+  for (int li = xcd_remap(blockIdx.x, gridDim.x); li < n_items; li += gridDim.x)
+    prefill_item<G, ONLINE, NW>(a, p0t, spt, rt, lds, li);
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt, const RopeTable& rt,
                           int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const int grid = a.B * a.Hkv * a.n_qtiles;
+  const int n_items = a.B * a.Hkv * a.n_qtiles;
+  const int one_per_cu = n_items < cu_count() ? n_items : cu_count();
+  // Local-layer items all cost about the same (window + query tile), so one
+  // workgroup per CU runs them back to back; global-layer items range from 1
+  // to S/64 key tiles and are left to the hardware's dynamic dispatch.  The
+  // online-maximum pass mostly finds nothing to redo: one workgroup per CU.
+  const int grid = a.local ? one_per_cu : n_items;
+  const int grid_online = one_per_cu;
   constexpr int NW = kPrefillWaves;
   const dim3 block(64 * NW);
   if (ev_start) hipEventRecord(ev_start, st);
@@ -704,10 +737,10 @@ hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const Span
   if (ev_stop) hipEventRecord(ev_stop, st);
   if (e != hipSuccess) return e;
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_fwd<1, true, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
-    case 2: hipLaunchKernelGGL((prefill_fwd<2, true, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
-    case 4: hipLaunchKernelGGL((prefill_fwd<4, true, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
-    case 8: hipLaunchKernelGGL((prefill_fwd<8, true, NW>), dim3(grid), block, 0, st, a, p0t, spt, rt); break;
+    case 1: hipLaunchKernelGGL((prefill_fwd<1, true, NW>), dim3(grid_online), block, 0, st, a, p0t, spt, rt); break;
+    case 2: hipLaunchKernelGGL((prefill_fwd<2, true, NW>), dim3(grid_online), block, 0, st, a, p0t, spt, rt); break;
+    case 4: hipLaunchKernelGGL((prefill_fwd<4, true, NW>), dim3(grid_online), block, 0, st, a, p0t, spt, rt); break;
+    case 8: hipLaunchKernelGGL((prefill_fwd<8, true, NW>), dim3(grid_online), block, 0, st, a, p0t, spt, rt); break;
   }
   return hipGetLastError();
 }
