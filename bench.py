@@ -155,17 +155,20 @@ def build_chunked_leg(torch, G, W, C):
     return leg
 
 
-def run_leg(torch, G, leg, timed):
-    """Launch the leg's layers; with timing, events bracket the leg and each
-    layer's main kernel (recorded by the library on the launch stream)."""
+def run_leg(torch, G, leg, timed, per_kernel=False):
+    """Launch the leg's layers.  timed: events bracket the whole leg.
+    per_kernel: events bracket each layer's main kernel (recorded by the
+    library on the launch stream); kept out of the leg-timed steps because the
+    extra event packets between kernels lengthen the leg itself."""
     if timed:
         leg.ev_leg[0].record()
     for l, call in enumerate(leg.calls):
-        if timed:
+        if per_kernel:
             G.set_timing_events(*leg.main_ev[l])
         call()
-    if timed:
+    if per_kernel:
         G.set_timing_events(None, None)
+    if timed:
         leg.ev_leg[1].record()
 
 
@@ -260,12 +263,20 @@ def main():
         torch.cuda.synchronize()
         for leg in legs:
             leg_ms[leg.name] += leg.ev_leg[0].elapsed_time(leg.ev_leg[1])
-            for l in range(LAYERS):
-                main_ms[leg.name][l] += leg.main_ev[l][0].elapsed_time(leg.main_ev[l][1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     K = max(args.steps, 1)
     print(f"[bench] timed {args.steps} steps in {wall:.2f} s", file=sys.stderr, flush=True)
+    # per-kernel durations (roofline), in steps of their own
+    KK = max(3, args.steps // 2)
+    for s in range(KK):
+        for leg in legs:
+            run_leg(torch, G, leg, timed=False, per_kernel=True)
+        torch.cuda.synchronize()
+        for leg in legs:
+            for l in range(LAYERS):
+                main_ms[leg.name][l] += leg.main_ev[l][0].elapsed_time(leg.main_ev[l][1])
+    print(f"[bench] {KK} steps of per-kernel timing done", file=sys.stderr, flush=True)
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -284,7 +295,7 @@ def main():
         ms = leg_ms["prefill"] / K
         flops = sum(leg.work)
         out["value"] = flops / (ms * 1e-3) / 1e12
-        kms = [x / K for x in main_ms["prefill"]]
+        kms = [x / KK for x in main_ms["prefill"]]
         achieved = flops / (sum(kms) * 1e-3) / 1e12
         out["config"] = {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                          "layers": "LLLLLG", "window": W.WINDOW, "rope_base": [W.ROPE_BASE_LOCAL, W.ROPE_BASE_GLOBAL],
@@ -298,7 +309,7 @@ def main():
         w = leg.workload
         ms = leg_ms["decode"] / K
         nbytes = sum(leg.work)
-        kms = [x / K for x in main_ms["decode"]]
+        kms = [x / KK for x in main_ms["decode"]]
         # split-K kernel: KV bytes only (q/o/new rows are handled around it)
         kv_bytes = [b - 2.0 * w.D * (2 * w.B * w.Hq + 2 * w.B * w.Hkv) for b in leg.work]
         ach = sum(kv_bytes) / (sum(kms) * 1e-3) / 1e9
@@ -312,7 +323,7 @@ def main():
         leg = by["chunked"]
         ms = leg_ms["chunked"] / K
         flops = sum(leg.work)
-        kms = [x / K for x in main_ms["chunked"]]
+        kms = [x / KK for x in main_ms["chunked"]]
         out["chunked_prefill"] = {"value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
                                   "workload": leg.workload.name, "ms": ms, "in_window_flop_per_block": flops,
                                   "kernel_TFLOPs": flops / (sum(kms) * 1e-3) / 1e12, "launch_ms": kms}
