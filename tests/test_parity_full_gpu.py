@@ -152,3 +152,26 @@ def test_mixed_mask_4k_full_heads(kind):
             ref = _oracle_rows(inp["q"][b, :, h], pos, kh, pos, inp["v"][b, :, g], kind, W.WINDOW, base, 1.0,
                                inp["q_gamma"], W.EPS, spans[b])
             assert_parity(_h(o[b, :, h]), ref, f"mixed mask b={b} h={h} kind={kind}")
+
+
+def test_local_uneven_items_per_workgroup():
+    """Local layer with 16 kv heads x 33 query tiles = 528 work items: with one
+    workgroup per CU some workgroups run one item more than others (and the
+    last query tile is ragged).  Every row of four heads against the oracle."""
+    B, S, Hq, Hkv, D = 1, 33 * 128 - 40, 32, 16, 128
+    rng = np.random.default_rng(77)
+    q = W.bf16_round(rng.standard_normal((B, S, Hq, D)).astype(np.float32))
+    k = W.bf16_round(rng.standard_normal((B, S, Hkv, D)).astype(np.float32))
+    v = W.bf16_round(rng.standard_normal((B, S, Hkv, D)).astype(np.float32))
+    gq = W.host_gamma(D, 78)
+    gk = W.host_gamma(D, 79)
+    dv = lambda x: torch.from_numpy(x).cuda().to(torch.bfloat16)  # noqa: E731
+    o = G.prefill(dv(q), dv(k), dv(v), G.LOCAL, W.WINDOW, W.ROPE_BASE_LOCAL, 1.0, torch.from_numpy(gq).cuda(),
+                  torch.from_numpy(gk).cuda(), W.EPS)
+    torch.cuda.synchronize()
+    pos = np.arange(S)
+    for h in (0, 9, 22, 31):
+        g = h // (Hq // Hkv)
+        kh = A.qknorm_rope(k[0, :, g:g + 1], gk, W.EPS, pos, W.ROPE_BASE_LOCAL, 1.0)[:, 0, :]
+        ref = _oracle_rows(q[0, :, h], pos, kh, pos, v[0, :, g], G.LOCAL, W.WINDOW, W.ROPE_BASE_LOCAL, 1.0, gq, W.EPS)
+        assert_parity(_h(o[0, :, h]), ref, f"uneven local h={h}")
