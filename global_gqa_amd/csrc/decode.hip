@@ -195,6 +195,10 @@ __global__ __launch_bounds__(256) void decode_splitk(DecodeArgs a, RopeTable rt)
     if (a.local && s_end - 1 < p - a.window + 1) empty = true;
   }
   if (empty) {
+    if (a.n_chunks == 1) {  // (unreachable: the token's own slot is visible)
+      for (int x = tid; x < G * kD; x += 256) a.o[((long long)b * a.Hq + g * G) * kD + x] = 0;
+      return;
+    }
     for (int x = tid; x < G * (kD + 2); x += 256) {
       const int hg = x / (kD + 2), e = x - hg * (kD + 2);
       part[hg * head_stride + e] = (e == kD) ? -__builtin_huge_valf() : 0.f;
@@ -278,6 +282,13 @@ __global__ __launch_bounds__(256) void decode_splitk(DecodeArgs a, RopeTable rt)
         den += wgt * part_l[i >> 2][i & 3][h];
       }
     }
+    if (a.n_chunks == 1) {
+      // a single split is the whole answer (the merge below would weigh it by
+      // exp2(0) = 1): normalise and store o here, no merge pass
+      const float o = den > 0.f ? num / den : 0.f;
+      a.o[((long long)b * a.Hq + g * G + h) * kD + d] = (uint16_t)(pack2(o, 0.f) & 0xffffu);
+      continue;
+    }
     part[h * head_stride + d] = num;
     if (d == 0) {
       part[h * head_stride + kD] = (den > 0.f) ? M : NEG_INF;
@@ -323,7 +334,7 @@ hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStr
   }
   hipError_t e = hipGetLastError();
   if (ev_stop) hipEventRecord(ev_stop, st);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.n_chunks == 1) return e;
   hipLaunchKernelGGL(decode_combine, dim3(a.B * a.Hq), dim3(128), 0, st, a);
   return hipGetLastError();
 }

@@ -37,8 +37,10 @@ def test_workspace_sizes(L):
     assert L.g3attn_prefill_workspace_size(0, 8192, 32, 16, 128) == 0
     ring = G.KVCacheC(0, 0, 1024, 1)
     lin = G.KVCacheC(0, 0, 40000, 0)
-    # ring: 4 splits of 256 slots; linear: positions 0..32768 in splits of 4096 -> 9
-    assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(ring)) == 32 * 32 * 4 * 130 * 4
+    # ring: one split (512 sequence x kv-head pairs); linear: positions 0..32768 in splits of 4096 -> 9
+    assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(ring)) == 32 * 32 * 1 * 130 * 4
+    # fewer pairs: the ring splits 4 ways (256 slots each)
+    assert L.g3attn_decode_workspace_size(2, 32, 16, 128, 32768, ctypes.byref(ring)) == 2 * 32 * 4 * 130 * 4
     assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(lin)) == 32 * 32 * 9 * 130 * 4
 
 
