@@ -214,14 +214,10 @@ __device__ __forceinline__ bf16x8 read_v(const uint16_t* vl, const TileAddr& ad,
 // of this one (if DO_QK), 16 + 16 MFMAs.  LDS operand reads run two PV steps
 // (256 MFMA cycles) or four QK steps ahead of the MFMAs that use them, and
 // scheduling fences keep the compiler from pulling them back next to their
-// uses, where each MFMA would wait out a full LDS latency.
-// The matrix half of a tile step: PV of the previous tile (if DO_PV) then QK
-// of this one (if DO_QK), 16 + 16 MFMAs.  LDS operand reads run two PV steps
-// (256 MFMA cycles) or four QK steps ahead of the MFMAs that use them, and
-// scheduling fences keep the compiler from pulling them back next to their
 // uses, where each MFMA would wait out a full LDS latency.  dma(k), k = 0..7,
-// issues the wave's share of the next tile's global->LDS loads, spread
-// between the MFMA groups so each waits for the memory pipeline on its own.
+// is a hook between the MFMA groups for global->LDS loads; the tile loop
+// passes an empty one (its loads go out at the end of the softmax half, which
+// measured faster than any placement between the MFMAs).
 template <bool DO_PV, bool DO_QK, typename Dma>
 __device__ __forceinline__ void gemm_half(const uint16_t* vl, const uint16_t* kl, const TileAddr& ad,
                                           const bf16x8 (&pb)[4], const bf16x8 (&q)[8], f32x16 (&s)[2],
@@ -696,8 +692,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW)
 void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[7 * kTileElems];
   const int n_items = a.B * a.Hkv * a.n_qtiles;
-  for (int li = xcd_remap(blockIdx.x, gridDim.x); li < n_items; li += gridDim.x)
-    prefill_item<G, ONLINE, NW>(a, p0t, spt, rt, lds, li);
+  const int li0 = xcd_remap(blockIdx.x, gridDim.x);
+  if (ONLINE) {
+    // The online-maximum pass usually finds nothing to redo: every wave reads
+    // the flags of all of this workgroup's items at once (one per lane) and
+    // the workgroup leaves unless one is set.
+    int any = 0;
+    for (int li = li0 + (int)(threadIdx.x & 63) * (int)gridDim.x; li < n_items; li += 64 * (int)gridDim.x)
+      any |= a.flags[li];
+    if (__builtin_amdgcn_ballot_w64(any != 0) == 0) return;
+  }
+  for (int li = li0; li < n_items; li += gridDim.x) prefill_item<G, ONLINE, NW>(a, p0t, spt, rt, lds, li);
 }
 
 // Compute units of the current device (cached per device).
