@@ -10,6 +10,9 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   * chunked leg  : a 4096-query chunk at positions 126976..131071 against a
                    131072-position cache (global, RoPE base 1e6 with position
                    interpolation 8) plus the five local layers.
+Beside the steps, once: the whole 62-layer 27B attention stack (52 local,
+10 global) over one 128K sequence, the prompt through chunked prefills of
+4096 tokens and then a decode loop, on per-layer caches (``schedule``).
 `value` is the prefill leg's in-window TFLOP/s (4*D flops per visible
 (query head, key) pair over the leg's wall time on the GPU); the decode
 leg's KV GB/s and the chunked leg's TFLOP/s are reported beside it.
@@ -43,6 +46,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="prefill,decode,chunked")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle-on-host baseline")
+    ap.add_argument("--no-schedule", action="store_true", help="skip the 62-layer 128K schedule run")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -170,6 +174,78 @@ def run_leg(torch, G, leg, timed, per_kernel=False):
         G.set_timing_events(None, None)
     if timed:
         leg.ev_leg[1].record()
+
+
+def run_schedule(torch, G, W, C, n_layers=62, total=131072, chunk=4096, n_decode=32):
+    """One 128K sequence through the whole 27B attention stack: a prompt of
+    total - n_decode tokens in chunks, then n_decode decode steps (the last at
+    position total - 1).  Synthetic raw q/k/v, two sets alternating by layer;
+    each layer's cache is written by its own calls."""
+    from global_gqa_amd.schedule import AttentionStack, chunk_bounds
+
+    w = W.WORKLOADS[2]
+    Hq, Hkv, D = w.Hq, w.Hkv, w.D
+    stack = AttentionStack(n_layers, 1, Hq, Hkv, max_positions=total, max_chunk=chunk, D=D, window=W.WINDOW,
+                           global_interp_scale=8.0, eps=W.EPS)
+    pre = [(W.device_normal_bf16((1, chunk, Hq, D), W.seed_of(6, i, W.T_Q)),
+            W.device_normal_bf16((1, chunk, Hkv, D), W.seed_of(6, i, W.T_K)),
+            W.device_normal_bf16((1, chunk, Hkv, D), W.seed_of(6, i, W.T_V))) for i in range(2)]
+    dec = [(W.device_normal_bf16((1, Hq, D), W.seed_of(6, 10 + i, W.T_Q)),
+            W.device_normal_bf16((1, Hkv, D), W.seed_of(6, 10 + i, W.T_K)),
+            W.device_normal_bf16((1, Hkv, D), W.seed_of(6, 10 + i, W.T_V))) for i in range(2)]
+    o_pre = torch.empty_like(pre[0][0])
+    o_dec = torch.empty_like(dec[0][0])
+    prompt = total - n_decode
+    bounds = chunk_bounds(prompt, chunk)
+    flops = 0.0
+    for (s0, e0) in bounds:
+        for p in stack.plans:
+            flops += C.prefill_flops(1, e0 - s0, Hq, D, p.kind == G.LOCAL, p.window, pos0=[s0], has_cache=True,
+                                     ring_capacity=p.capacity if p.is_ring else None)
+    nbytes_tok = [sum(C.decode_bytes(1, Hq, Hkv, D, [prompt + t], p.kind == G.LOCAL, p.window) for p in stack.plans)
+                  for t in range(n_decode)]
+    n_eager = n_decode // 4
+    ev = _events(torch, 4)
+    torch.cuda.synchronize()
+    ev[0][0].record()
+    for (s0, e0) in bounds:
+        n = e0 - s0
+        for i in range(n_layers):
+            q, k, v = pre[i & 1]
+            stack.prefill_layer(i, q[:, :n], k[:, :n], v[:, :n], o=o_pre[:, :n])
+        stack.advance(n)
+    ev[0][1].record()
+    # decode: the first tokens with eager calls, the rest by replaying one
+    # captured graph of the 62 layers' calls (a serving loop's form)
+    for t in range(n_eager):
+        for i in range(n_layers):
+            q, k, v = dec[i & 1]
+            stack.decode_layer(i, q, k, v, o=o_dec)
+        stack.advance(1)
+    ev[1][1].record()
+    torch.cuda.synchronize()
+    step = stack.capture_decode([dec[i & 1][0] for i in range(n_layers)], [dec[i & 1][1] for i in range(n_layers)],
+                                [dec[i & 1][2] for i in range(n_layers)], [o_dec] * n_layers)
+    torch.cuda.synchronize()
+    ev[2][0].record()
+    for t in range(n_decode - n_eager):
+        step()
+    ev[2][1].record()
+    torch.cuda.synchronize()
+    ms_pre = ev[0][0].elapsed_time(ev[0][1])
+    ms_eager = ev[0][1].elapsed_time(ev[1][1])
+    ms_graph = ev[2][0].elapsed_time(ev[2][1])
+    b_eager = sum(nbytes_tok[:n_eager])
+    b_graph = sum(nbytes_tok[n_eager:])
+    return {"workload": f"27b-{n_layers}-layer-128k: prompt {prompt} tokens in chunks of {chunk}, then "
+                        f"{n_decode} decode steps (positions {prompt}..{total - 1}), B=1",
+            "layers": n_layers, "global_layers": sum(p.kind == G.GLOBAL for p in stack.plans),
+            "prompt_ms": ms_pre, "prompt_in_window_flop": flops, "prompt_TFLOPs": flops / (ms_pre * 1e-3) / 1e12,
+            "decode_ms_per_token": ms_graph / (n_decode - n_eager),
+            "decode_GBs": b_graph / (ms_graph * 1e-3) / 1e9,
+            "decode_eager_ms_per_token": ms_eager / n_eager,
+            "decode_eager_GBs": b_eager / (ms_eager * 1e-3) / 1e9,
+            "decode_bytes_per_token": b_graph / (n_decode - n_eager)}
 
 
 def cpu_baseline(torch, W, C, prefill_leg):
@@ -329,6 +405,9 @@ def main():
                                   "kernel_TFLOPs": flops / (sum(kms) * 1e-3) / 1e12, "launch_ms": kms}
     if out["value"] is None:
         out["value"] = 0.0
+    if not args.no_schedule:
+        print("[bench] 62-layer 128K schedule...", file=sys.stderr, flush=True)
+        out["schedule_27b_128k"] = run_schedule(torch, G, W, C)
     if not args.no_cpu_baseline and "prefill" in by:
         print("[bench] cpu baseline (oracle on host)...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(torch, W, C, by["prefill"])

@@ -298,26 +298,56 @@ __global__ __launch_bounds__(256) void decode_splitk(DecodeArgs a, RopeTable rt)
 }
 
 // Merge the split-K partials of one head: o = sum_c w_c o_c / sum_c w_c l_c
-// with w_c = exp2(m_c - M) (maxima are in log2 units), splits in ascending
-// order, so the result is bitwise reproducible.
-__global__ __launch_bounds__(128) void decode_combine(DecodeArgs a) {
+// with w_c = exp2(m_c - M) (maxima are in log2 units).  kCombineGroups
+// groups of 128 threads (one per dim) take the splits c = j, j + groups, ...
+// with a running maximum, then thread group 0 merges the groups' (M, num,
+// den) in group order: a fixed order, so the result is bitwise
+// reproducible, and a long cache's hundreds of splits are read by many
+// threads at once instead of one after another.
+constexpr int kCombineGroups = 8;
+__global__ __launch_bounds__(128 * kCombineGroups) void decode_combine(DecodeArgs a) {
+  __shared__ float gm[kCombineGroups], gnum[kCombineGroups][kD], gden[kCombineGroups];
   const int h = blockIdx.x;  // b * Hq + head
-  const int d = threadIdx.x;
+  const int d = threadIdx.x & (kD - 1);
+  const int grp = threadIdx.x >> 7;
   const float* part = a.ws + (long long)h * a.n_chunks * (kD + 2);
   const float NEG_INF = -__builtin_huge_valf();
-  float M = NEG_INF;
-  for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, part[c * (kD + 2) + kD]);
-  float num = 0.f, den = 0.f;
-  if (M != NEG_INF) {
-    for (int c = 0; c < a.n_chunks; ++c) {
-      const float mc = part[c * (kD + 2) + kD];
-      if (mc == NEG_INF) continue;
-      const float w = fast_exp2(mc - M);
-      num += w * part[c * (kD + 2) + d];
-      den += w * part[c * (kD + 2) + kD + 1];
+  float M = NEG_INF, num = 0.f, den = 0.f;
+  for (int c = grp; c < a.n_chunks; c += kCombineGroups) {
+    const float* pc = part + (long long)c * (kD + 2);
+    const float mc = pc[kD];
+    if (mc == NEG_INF) continue;
+    if (mc > M) {
+      const float r = (M == NEG_INF) ? 0.f : fast_exp2(M - mc);
+      num *= r;
+      den *= r;
+      M = mc;
+    }
+    const float w = fast_exp2(mc - M);
+    num += w * pc[d];
+    den += w * pc[kD + 1];
+  }
+  gnum[grp][d] = num;
+  if (d == 0) {
+    gm[grp] = M;
+    gden[grp] = den;
+  }
+  __syncthreads();
+  if (grp != 0) return;
+  float MM = NEG_INF;
+#pragma unroll
+  for (int g = 0; g < kCombineGroups; ++g) MM = fmaxf(MM, gm[g]);
+  float n2 = 0.f, d2 = 0.f;
+  if (MM != NEG_INF) {
+#pragma unroll
+    for (int g = 0; g < kCombineGroups; ++g) {
+      if (gm[g] == NEG_INF) continue;
+      const float w = fast_exp2(gm[g] - MM);
+      n2 += w * gnum[g][d];
+      d2 += w * gden[g];
     }
   }
-  const float o = den > 0.f ? num / den : 0.f;
+  const float o = d2 > 0.f ? n2 / d2 : 0.f;
   a.o[(long long)h * kD + d] = (uint16_t)(pack2(o, 0.f) & 0xffffu);
 }
 
@@ -335,7 +365,7 @@ hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStr
   hipError_t e = hipGetLastError();
   if (ev_stop) hipEventRecord(ev_stop, st);
   if (e != hipSuccess || a.n_chunks == 1) return e;
-  hipLaunchKernelGGL(decode_combine, dim3(a.B * a.Hq), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(decode_combine, dim3(a.B * a.Hq), dim3(128 * kCombineGroups), 0, st, a);
   return hipGetLastError();
 }
 

@@ -122,6 +122,40 @@ class AttentionStack:
                       p.rope_base, p.interp_scale, self.q_gammas[i], self.k_gammas[i], self.eps,
                       self.softmax_scale, o=o, workspace=self.decode_ws, stream=stream)
 
+    def capture_decode(self, q_bufs, k_bufs, v_bufs, o_bufs):
+        """Capture one decode step of every layer (layer i reads q_bufs[i],
+        k_bufs[i], v_bufs[i] and writes o_bufs[i]) followed by the position
+        increment into a HIP graph, and return a function that replays it for
+        the token at the current position.  The library's calls allocate
+        nothing and issue no memsets, so the captured launches replay as they
+        are; the caller refills the input buffers between replays."""
+        import torch
+
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(self.n_layers):
+                    self.decode_layer(i, q_bufs[i], k_bufs[i], v_bufs[i], o=o_bufs[i])
+                self.positions.add_(1)
+        torch.cuda.current_stream().wait_stream(side)
+
+        def step():
+            if self.pos >= self.max_positions:
+                raise ValueError(f"position {self.pos} exceeds max_positions={self.max_positions}")
+            g.replay()
+            self.pos += 1
+
+        step.graph = g  # keeps the graph alive with the function
+        return step
+
+    def reset(self):
+        """Start a new prompt: position 0 (old cache contents are never read
+        again: every later read is of a position written after the reset)."""
+        self.pos = 0
+        self.positions.fill_(0)
+
     def advance(self, n: int):
         """Every layer has processed the next n positions."""
         if n < 0 or self.pos + n > self.max_positions:

@@ -75,6 +75,53 @@ def test_stack_prompt_then_decode(B, Hq, Hkv, chunks, n_decode):
             assert_rowwise_bf16(ck[b][:, slots, :], kh.transpose(1, 0, 2), f"layer {l} cache k")
 
 
+def test_stack_decode_graph_replays():
+    """The decode step of every layer captured once in a HIP graph and
+    replayed token after token (inputs refilled and outputs read back with
+    eager work and synchronisations between replays) gives the oracle's rows,
+    like the eager calls."""
+    n_layers, B, Hq, Hkv, D = 7, 1, 4, 2, 128
+    prompt, n_decode = 1100, 4  # the ring has wrapped before the first decoded token
+    N = prompt + n_decode
+    layers = []
+    for l in range(n_layers):
+        layers.append(tuple(W.host_normal_bf16(shape, W.seed_of(CONFIG + 1, l, t)) for shape, t in
+                            [((B, N, Hq, D), W.T_Q), ((B, N, Hkv, D), W.T_K), ((B, N, Hkv, D), W.T_V)]) +
+                      (W.host_gamma(D, W.seed_of(CONFIG + 1, l, W.T_GQ)), W.host_gamma(D, W.seed_of(CONFIG + 1, l, W.T_GK))))
+    stack = AttentionStack(n_layers, B, Hq, Hkv, max_positions=N, max_chunk=prompt, global_interp_scale=8.0,
+                           q_gammas=[dev_f32(x[3]) for x in layers], k_gammas=[dev_f32(x[4]) for x in layers],
+                           eps=W.EPS)
+    for l, (q, k, v, _, _) in enumerate(layers):
+        stack.prefill_layer(l, dev_bf16(q[:, :prompt]), dev_bf16(k[:, :prompt]), dev_bf16(v[:, :prompt]))
+    stack.advance(prompt)
+    qb = [torch.zeros((B, Hq, D), dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
+    kb = [torch.zeros((B, Hkv, D), dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
+    vb = [torch.zeros((B, Hkv, D), dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
+    ob = [torch.zeros((B, Hq, D), dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
+    torch.cuda.synchronize()
+    step = stack.capture_decode(qb, kb, vb, ob)
+    torch.cuda.synchronize()
+    assert stack.pos == prompt and int(stack.positions[0]) == prompt  # capture ran nothing
+    got = np.zeros((n_layers, B, n_decode, Hq, D))
+    for t in range(n_decode):
+        p = prompt + t
+        for l, (q, k, v, _, _) in enumerate(layers):
+            qb[l].copy_(dev_bf16(q[:, p]))
+            kb[l].copy_(dev_bf16(k[:, p]))
+            vb[l].copy_(dev_bf16(v[:, p]))
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            got[l, :, t] = host(ob[l])
+    assert stack.pos == N and int(stack.positions[0]) == N
+    for l, (q, k, v, gq, gk) in enumerate(layers):
+        plan = stack.plans[l]
+        ref = A.prefill(q, k, v, plan.kind, plan.window, plan.rope_base, plan.interp_scale, gq, gk, W.EPS)
+        for t in range(n_decode):
+            assert_parity(got[l, :, t], ref[:, prompt + t], f"layer {l} graph replay {t}")
+
+
 def test_stack_rejects_positions_past_capacity():
     stack = AttentionStack(6, 1, 2, 1, max_positions=100, max_chunk=64)
     x = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16, device="cuda")
