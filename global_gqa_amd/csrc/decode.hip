@@ -14,7 +14,7 @@
 // flight.  Sixteen lanes share a key row (8 dims each, DPP row reductions)
 // and all G heads of the group use every row.  The partial (o, m, l) of the
 // split goes to the workspace; a second kernel merges the partials of a head
-// in ascending split order, so results are bitwise reproducible.
+// in a fixed order, so results are bitwise reproducible.
 #include "g3_common.hpp"
 #include "g3_kernels.hpp"
 
