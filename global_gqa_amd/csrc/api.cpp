@@ -28,8 +28,10 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool head_dim_ok(int32_t D) { return D == 128 || D == 256; }
+
 int check_heads(int32_t Hq, int32_t Hkv, int32_t D) {
-  if (D != g3::kD) return fail(G3_EUNSUPPORTED, "head dim D=%d not supported (only 128)", D);
+  if (!head_dim_ok(D)) return fail(G3_EUNSUPPORTED, "head dim D=%d not supported (128 or 256)", D);
   if (Hq <= 0 || Hkv <= 0) return fail(G3_EINVAL, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
   if (Hq % Hkv) return fail(G3_EINVAL, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   const int G = Hq / Hkv;
@@ -46,10 +48,10 @@ int check_rope(float rope_base, float interp_scale, float eps) {
   return G3_OK;
 }
 
-int check_scale(float softmax_scale, float* sl2) {
+int check_scale(float softmax_scale, int32_t D, float* sl2) {
   if (softmax_scale < 0.0f || !std::isfinite(softmax_scale))
     return fail(G3_EINVAL, "softmax_scale must be >= 0 (0 = D^-1/2), got %g", softmax_scale);
-  const float s = softmax_scale == 0.0f ? 1.0f / std::sqrt((float)g3::kD) : softmax_scale;
+  const float s = softmax_scale == 0.0f ? 1.0f / std::sqrt((float)D) : softmax_scale;
   *sl2 = s * 1.4426950408889634f;
   return G3_OK;
 }
@@ -57,22 +59,23 @@ int check_scale(float softmax_scale, float* sl2) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // RoPE frequencies base^(-2k/D), in revolutions per (interpolated) position.
-g3::RopeTable rope_table(float base, float interp_scale) {
-  g3::RopeTable t;
+g3::RopeTable rope_table(float base, float interp_scale, int D) {
+  g3::RopeTable t{};
   const double inv2pi = 0.15915494309189533576888376337251;
-  for (int k = 0; k < g3::kD / 2; ++k)
-    t.rev[k] = std::pow((double)base, -2.0 * k / g3::kD) * inv2pi / (double)interp_scale;
+  for (int k = 0; k < D / 2; ++k)
+    t.rev[k] = std::pow((double)base, -2.0 * k / D) * inv2pi / (double)interp_scale;
   return t;
 }
 
 // Prefill workspace: normed+rotated chunk keys [B][Hkv][S][D] bf16, then one
-// int32 flag per flash workgroup (sized for the smallest tile, G = 1).
+// int32 flag per flash work item, sized for the most items any group size
+// can give (G = 8 query heads per kv head).
 size_t prefill_ws_keys(int32_t B, int32_t S, int32_t Hkv, int32_t D) {
   return round_up((size_t)B * Hkv * S * D * sizeof(uint16_t), 256);
 }
 size_t prefill_ws(int32_t B, int32_t S, int32_t Hkv, int32_t D) {
-  const size_t tiles = (size_t)B * Hkv * ((S + g3::prefill_rows_per_wg(1) - 1) / g3::prefill_rows_per_wg(1)) *
-                       (size_t)8;  // up to 8 query heads per kv head
+  const int rows1 = D == 256 ? g3::prefill_rows_per_wg_d256(1) : g3::prefill_rows_per_wg(1);
+  const size_t tiles = (size_t)B * Hkv * ((S + rows1 - 1) / rows1) * (size_t)8;
   return prefill_ws_keys(B, S, Hkv, D) + round_up(tiles * sizeof(int32_t), 256);
 }
 
@@ -103,8 +106,8 @@ int decode_chunks(int n_slots, int32_t B, int32_t Hkv) {
   return (n_slots + split - 1) / split;
 }
 
-size_t decode_ws(int32_t B, int32_t Hq, int n_chunks) {
-  return round_up((size_t)B * Hq * n_chunks * (g3::kD + 2) * sizeof(float), 256);
+size_t decode_ws(int32_t B, int32_t Hq, int32_t D, int n_chunks) {
+  return round_up((size_t)B * Hq * n_chunks * (D + 2) * sizeof(float), 256);
 }
 
 }  // namespace
@@ -130,7 +133,7 @@ int g3attn_qknorm_rope(const g3_bf16* q_in, const g3_bf16* k_in, g3_bf16* q_out,
                        int32_t T, int32_t Hq, int32_t Hkv, int32_t D, float rope_base, float interp_scale,
                        void* stream) {
   g_err[0] = 0;
-  if (D != g3::kD) return fail(G3_EUNSUPPORTED, "head dim D=%d not supported (only 128)", D);
+  if (!head_dim_ok(D)) return fail(G3_EUNSUPPORTED, "head dim D=%d not supported (128 or 256)", D);
   if (T < 0) return fail(G3_EINVAL, "T=%d < 0", T);
   if ((q_in == nullptr) != (q_out == nullptr)) return fail(G3_EINVAL, "q_in and q_out must both be set or NULL");
   if ((k_in == nullptr) != (k_out == nullptr)) return fail(G3_EINVAL, "k_in and k_out must both be set or NULL");
@@ -158,7 +161,8 @@ int g3attn_qknorm_rope(const g3_bf16* q_in, const g3_bf16* k_in, g3_bf16* q_out,
     a.H = which ? Hkv : Hq;
     a.S = T;
     a.head_major = 0;
-    if (hipError_t e = g3::launch_qknorm_rope(a, p0t, rope_table(rope_base, interp_scale), st))
+    a.D = D;
+    if (hipError_t e = g3::launch_qknorm_rope(a, p0t, rope_table(rope_base, interp_scale, D), st))
       return fail(G3_EHIP, "qknorm_rope launch failed: %s", hipGetErrorString(e));
   }
   return G3_OK;
@@ -182,7 +186,7 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
   if (layer_kind == G3_LOCAL && window < 1) return fail(G3_EINVAL, "window=%d < 1", window);
   if (int e = check_rope(rope_base, interp_scale, eps)) return e;
   float sl2;
-  if (int e = check_scale(softmax_scale, &sl2)) return e;
+  if (int e = check_scale(softmax_scale, D, &sl2)) return e;
   if (!q || !k || !v || !o) return fail(G3_EINVAL, "q, k, v and o must be non-NULL");
   for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o})
     if (!aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
@@ -249,7 +253,7 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
 
   hipStream_t st = (hipStream_t)stream;
   uint16_t* khat = (uint16_t*)workspace;
-  const g3::RopeTable rt = rope_table(rope_base, interp_scale);
+  const g3::RopeTable rt = rope_table(rope_base, interp_scale, D);
   {
     g3::RowsArgs a{};
     a.in = k;
@@ -261,6 +265,7 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
     a.H = Hkv;
     a.S = S;
     a.head_major = 1;
+    a.D = D;
     if (hipError_t e = g3::launch_qknorm_rope(a, p0t, rt, st))
       return fail(G3_EHIP, "k prologue launch failed: %s", hipGetErrorString(e));
   }
@@ -285,11 +290,12 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
   a.local = layer_kind == G3_LOCAL;
   a.window = layer_kind == G3_LOCAL ? window : (1 << 30);
   a.sl2 = sl2;
-  const int rows = g3::prefill_rows_per_wg(G);
+  const int rows = D == 256 ? g3::prefill_rows_per_wg_d256(G) : g3::prefill_rows_per_wg(G);
   a.n_qtiles = (S + rows - 1) / rows;
   if ((long long)B * Hkv * a.n_qtiles > (1LL << 31) - 1) return fail(G3_EINVAL, "grid too large");
-  if (hipError_t e = g3::launch_prefill(a, p0t, spt, rt, G, st, g_ev_start, g_ev_stop))
-    return fail(G3_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
+  const hipError_t le = D == 256 ? g3::launch_prefill_d256(a, p0t, spt, rt, G, st, g_ev_start, g_ev_stop)
+                                 : g3::launch_prefill(a, p0t, spt, rt, G, st, g_ev_start, g_ev_stop);
+  if (le != hipSuccess) return fail(G3_EHIP, "prefill launch failed: %s", hipGetErrorString(le));
   if (cache) {
     g3::AppendArgs ap{};
     ap.khat = khat;
@@ -301,6 +307,7 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
     ap.Hkv = Hkv;
     ap.cap = cache->capacity;
     ap.is_ring = cache->is_ring;
+    ap.D = D;
     if (hipError_t e = g3::launch_append_chunk(ap, p0t, st))
       return fail(G3_EHIP, "cache append launch failed: %s", hipGetErrorString(e));
   }
@@ -309,9 +316,9 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
 
 size_t g3attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_position,
                                     const g3_kv_cache* cache) {
-  (void)D;
-  if (!cache || B <= 0 || Hq <= 0 || Hkv <= 0 || max_position < 0 || cache->capacity <= 0) return 0;
-  return decode_ws(B, Hq, decode_chunks(decode_slots(cache, max_position), B, Hkv));
+  if (!cache || B <= 0 || Hq <= 0 || Hkv <= 0 || max_position < 0 || cache->capacity <= 0 || !head_dim_ok(D))
+    return 0;
+  return decode_ws(B, Hq, D, decode_chunks(decode_slots(cache, max_position), B, Hkv));
 }
 
 int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, g3_bf16* o, int32_t B, int32_t Hq,
@@ -326,7 +333,7 @@ int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, 
   if (layer_kind == G3_LOCAL && window < 1) return fail(G3_EINVAL, "window=%d < 1", window);
   if (int e = check_rope(rope_base, interp_scale, eps)) return e;
   float sl2;
-  if (int e = check_scale(softmax_scale, &sl2)) return e;
+  if (int e = check_scale(softmax_scale, D, &sl2)) return e;
   if (!q || !k_new || !v_new || !o || !positions) return fail(G3_EINVAL, "q, k_new, v_new, o, positions must be non-NULL");
   for (const void* p : {(const void*)q, (const void*)k_new, (const void*)v_new, (const void*)o})
     if (!aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
@@ -343,7 +350,7 @@ int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, 
   const int n_slots = decode_slots(cache, max_position);
   const int split = decode_split(n_slots, B, Hkv);
   const int n_chunks = decode_chunks(n_slots, B, Hkv);
-  const size_t need = decode_ws(B, Hq, n_chunks);
+  const size_t need = decode_ws(B, Hq, D, n_chunks);
   if (!workspace || workspace_bytes < need)
     return fail(G3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(G3_EINVAL, "workspace must be 256-byte aligned");
@@ -373,7 +380,8 @@ int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, 
   a.split = split;
   a.n_chunks = n_chunks;
   a.sl2 = sl2;
-  if (hipError_t e = g3::launch_decode(a, rope_table(rope_base, interp_scale), Hq / Hkv, (hipStream_t)stream,
+  a.D = D;
+  if (hipError_t e = g3::launch_decode(a, rope_table(rope_base, interp_scale, D), Hq / Hkv, (hipStream_t)stream,
                                        g_ev_start, g_ev_stop))
     return fail(G3_EHIP, "decode launch failed: %s", hipGetErrorString(e));
   return G3_OK;

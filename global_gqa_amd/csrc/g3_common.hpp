@@ -6,7 +6,8 @@
 
 namespace g3 {
 
-constexpr int kD = 128;          // head dimension handled by the kernels
+constexpr int kD = 128;          // head dimension of the 27B-shaped kernels
+constexpr int kDMax = 256;       // largest head dimension (Gemma 3 1B)
 constexpr int kMaxSpans = 64;    // image spans per call (kernel-argument table)
 constexpr int kMaxBatchPos0 = 256;  // sequences per prefill call with explicit pos0
 
@@ -39,10 +40,11 @@ struct Pos0Table {
 
 __device__ __forceinline__ int pos0_of(const Pos0Table& t, int b) { return t.uniform ? t.v[0] : t.v[b]; }
 
-// RoPE frequencies of the 64 rotation pairs in revolutions per position,
-// base^(-2k/D) / (2 pi) / interp_scale, computed once per call in fp64.
+// RoPE frequencies of the D/2 rotation pairs in revolutions per position,
+// base^(-2k/D) / (2 pi) / interp_scale, computed once per call in fp64
+// (entries past D/2 unused).
 struct RopeTable {
-  double rev[kD / 2];
+  double rev[kDMax / 2];
 };
 
 // bf16 <-> f32 on packed 32-bit words (low half = element 0).

@@ -19,6 +19,7 @@ struct RowsArgs {
   float eps;
   int T, H, S;            // S: tokens per sequence (for pos0 and head-major)
   int head_major;
+  int D;                  // head dimension (128 or 256)
 };
 
 struct AppendArgs {
@@ -27,6 +28,7 @@ struct AppendArgs {
   uint16_t* ck;           // [B][Hkv][cap][D]
   uint16_t* cv;
   int B, S, Hkv, cap, is_ring;
+  int D;
 };
 
 struct PrefillArgs {
@@ -56,6 +58,7 @@ struct DecodeArgs {
   const float* q_gamma;
   const float* k_gamma;
   float* ws;              // [B][Hq][n_chunks][D + 2] partials (o, m, l)
+  int D;                  // head dimension (128 or 256)
   uint16_t* o;            // [B][Hq][D]
   float eps;
   int B, Hq, Hkv, cap, is_ring, local, window;
@@ -72,6 +75,9 @@ hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, const Rop
 hipError_t launch_append_chunk(const AppendArgs& a, const Pos0Table& p0t, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt, const RopeTable& rt,
                           int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+// Head dimension 256 (Gemma 3 1B): 4 waves x 32 query rows per workgroup.
+hipError_t launch_prefill_d256(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt,
+                               const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
 
@@ -82,5 +88,7 @@ hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStr
 constexpr int kPrefillWaves = G3_PREFILL_WAVES;
 // Tiles: positions per prefill workgroup for a GQA group of size G.
 inline int prefill_rows_per_wg(int G) { return kPrefillWaves * (32 / G); }
+constexpr int kPrefillWavesD256 = 4;
+inline int prefill_rows_per_wg_d256(int G) { return kPrefillWavesD256 * (32 / G); }
 
 }  // namespace g3

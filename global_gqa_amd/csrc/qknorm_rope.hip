@@ -6,25 +6,39 @@
 // (x_k, x_{k+64}) rotated by (p / s) * base^(-2k/128) (Technical Report,
 // section 2 "Long context": base 10k local / 1M global, linear position
 // interpolation on the global layers).  Memory bound: one read and one write
-// of each 256-byte head row.
+// of each head row (256 bytes at D = 128, 512 at D = 256).
 #include "g3_common.hpp"
 #include "g3_kernels.hpp"
 
 namespace g3 {
 
-// 16 lanes per head row; lane j owns dims [4j, 4j+4) and [64+4j, 64+4j+4),
-// so every rotation pair stays inside one lane.
-template <bool NORM>
+// 16 lanes per head row; lane j owns dims [E j, E j + E) and
+// [D/2 + E j, D/2 + E j + E) with E = D / 32 (4 for D = 128, 8 for D = 256),
+// so every rotation pair (k, k + D/2) stays inside one lane.
+template <int E>
+struct Vec;
+template <>
+struct Vec<4> {
+  typedef u32x2 T;
+};
+template <>
+struct Vec<8> {
+  typedef u32x4 T;
+};
+
+template <int D, bool NORM>
 __global__ __launch_bounds__(256) void qknorm_rope_rows(RowsArgs a, Pos0Table p0t, RopeTable rt) {
+  constexpr int E = D / 32;
+  typedef typename Vec<E>::T VT;
   const int j = threadIdx.x & 15;
-  double rev[4];
+  double rev[E];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rev[i] = rt.rev[4 * j + i];
-  float gam[8];
+  for (int i = 0; i < E; ++i) rev[i] = rt.rev[E * j + i];
+  float gam[2 * E];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    gam[i] = NORM ? a.gamma[4 * j + i] : 1.f;
-    gam[4 + i] = NORM ? a.gamma[64 + 4 * j + i] : 1.f;
+  for (int i = 0; i < E; ++i) {
+    gam[i] = NORM ? a.gamma[E * j + i] : 1.f;
+    gam[E + i] = NORM ? a.gamma[D / 2 + E * j + i] : 1.f;
   }
   const long long n_rows = (long long)a.T * a.H;
   const long long stride = (long long)gridDim.x * 16;
@@ -34,34 +48,46 @@ __global__ __launch_bounds__(256) void qknorm_rope_rows(RowsArgs a, Pos0Table p0
     const int bt = (int)(t / a.S);
     const int st = (int)(t - (long long)bt * a.S);
     const int pos = a.positions ? a.positions[t] : pos0_of(p0t, bt) + st;
-    const uint16_t* src = a.in + R * kD;
-    const u32x2 lo = *(const u32x2*)(src + 4 * j);
-    const u32x2 hi = *(const u32x2*)(src + 64 + 4 * j);
-    float x[8] = {bf_lo(lo[0]), bf_hi(lo[0]), bf_lo(lo[1]), bf_hi(lo[1]),
-                  bf_lo(hi[0]), bf_hi(hi[0]), bf_lo(hi[1]), bf_hi(hi[1])};
+    const uint16_t* src = a.in + R * D;
+    const VT lo = *(const VT*)(src + E * j);
+    const VT hi = *(const VT*)(src + D / 2 + E * j);
+    float x[2 * E];
+#pragma unroll
+    for (int e = 0; e < E / 2; ++e) {
+      x[2 * e] = bf_lo(lo[e]);
+      x[2 * e + 1] = bf_hi(lo[e]);
+      x[E + 2 * e] = bf_lo(hi[e]);
+      x[E + 2 * e + 1] = bf_hi(hi[e]);
+    }
     if (NORM) {
       float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+      for (int i = 0; i < 2 * E; ++i) ss += x[i] * x[i];
       ss += __shfl_xor(ss, 8, 16);
       ss += __shfl_xor(ss, 4, 16);
       ss += __shfl_xor(ss, 2, 16);
       ss += __shfl_xor(ss, 1, 16);
-      const float r = __frsqrt_rn(ss * (1.f / kD) + a.eps);
+      const float r = __frsqrt_rn(ss * (1.f / D) + a.eps);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = x[i] * r * gam[i];
+      for (int i = 0; i < 2 * E; ++i) x[i] = x[i] * r * gam[i];
     }
-    float y[8];
+    float y[2 * E];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < E; ++i) {
       float sn, cs;
       rope_sincos(pos, rev[i], sn, cs);
-      y[i] = x[i] * cs - x[4 + i] * sn;
-      y[4 + i] = x[i] * sn + x[4 + i] * cs;
+      y[i] = x[i] * cs - x[E + i] * sn;
+      y[E + i] = x[i] * sn + x[E + i] * cs;
     }
-    uint16_t* dst = a.out + (a.head_major ? (((long long)bt * a.H + h) * a.S + st) * kD : R * kD);
-    *(u32x2*)(dst + 4 * j) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
-    *(u32x2*)(dst + 64 + 4 * j) = u32x2{pack2(y[4], y[5]), pack2(y[6], y[7])};
+    uint16_t* dst = a.out + (a.head_major ? (((long long)bt * a.H + h) * a.S + st) * D : R * D);
+    VT wlo, whi;
+#pragma unroll
+    for (int e = 0; e < E / 2; ++e) {
+      wlo[e] = pack2(y[2 * e], y[2 * e + 1]);
+      whi[e] = pack2(y[E + 2 * e], y[E + 2 * e + 1]);
+    }
+    *(VT*)(dst + E * j) = wlo;
+    *(VT*)(dst + D / 2 + E * j) = whi;
   }
 }
 
@@ -70,10 +96,11 @@ __global__ __launch_bounds__(256) void qknorm_rope_rows(RowsArgs a, Pos0Table p0
 // of the chunk, so earlier rows (which would land on the same slots) are
 // skipped instead of racing.
 __global__ __launch_bounds__(256) void append_chunk(AppendArgs a, Pos0Table p0t) {
-  const long long n = (long long)a.B * a.Hkv * a.S * 16;
+  const int cpr = a.D / 8;  // 16-byte chunks per row
+  const long long n = (long long)a.B * a.Hkv * a.S * cpr;
   for (long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (long long)gridDim.x * blockDim.x) {
-    const int c16 = (int)(x & 15);
-    const long long row = x >> 4;  // (b, g, r)
+    const int c16 = (int)(x % cpr);
+    const long long row = x / cpr;  // (b, g, r)
     const int r = (int)(row % a.S);
     const long long bg = row / a.S;
     const int g = (int)(bg % a.Hkv);
@@ -81,9 +108,9 @@ __global__ __launch_bounds__(256) void append_chunk(AppendArgs a, Pos0Table p0t)
     if (a.is_ring && r < a.S - a.cap) continue;
     const int pos = pos0_of(p0t, b) + r;
     const long long slot = a.is_ring ? (pos % a.cap) : pos;
-    const long long dst = ((bg)*a.cap + slot) * kD + c16 * 8;
-    *(u32x4*)(a.ck + dst) = *(const u32x4*)(a.khat + row * kD + c16 * 8);
-    *(u32x4*)(a.cv + dst) = *(const u32x4*)(a.v + (((long long)b * a.S + r) * a.Hkv + g) * kD + c16 * 8);
+    const long long dst = ((bg)*a.cap + slot) * a.D + c16 * 8;
+    *(u32x4*)(a.ck + dst) = *(const u32x4*)(a.khat + row * a.D + c16 * 8);
+    *(u32x4*)(a.cv + dst) = *(const u32x4*)(a.v + (((long long)b * a.S + r) * a.Hkv + g) * a.D + c16 * 8);
   }
 }
 
@@ -98,15 +125,22 @@ hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, const Rop
   // a grid-stride loop over rows: at most 8 workgroups per CU
   long long grid = ((long long)a.T * a.H + 15) / 16;
   if (grid > 2048) grid = 2048;
-  if (a.gamma)
-    hipLaunchKernelGGL(qknorm_rope_rows<true>, dim3((int)grid), dim3(256), 0, st, a, p0t, rt);
-  else
-    hipLaunchKernelGGL(qknorm_rope_rows<false>, dim3((int)grid), dim3(256), 0, st, a, p0t, rt);
+  if (a.D == 256) {
+    if (a.gamma)
+      hipLaunchKernelGGL((qknorm_rope_rows<256, true>), dim3((int)grid), dim3(256), 0, st, a, p0t, rt);
+    else
+      hipLaunchKernelGGL((qknorm_rope_rows<256, false>), dim3((int)grid), dim3(256), 0, st, a, p0t, rt);
+  } else {
+    if (a.gamma)
+      hipLaunchKernelGGL((qknorm_rope_rows<128, true>), dim3((int)grid), dim3(256), 0, st, a, p0t, rt);
+    else
+      hipLaunchKernelGGL((qknorm_rope_rows<128, false>), dim3((int)grid), dim3(256), 0, st, a, p0t, rt);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_append_chunk(const AppendArgs& a, const Pos0Table& p0t, hipStream_t st) {
-  const int grid = grid_for((long long)a.B * a.Hkv * a.S * 16, 256);
+  const int grid = grid_for((long long)a.B * a.Hkv * a.S * (a.D / 8), 256);
   hipLaunchKernelGGL(append_chunk, dim3(grid), dim3(256), 0, st, a, p0t);
   return hipGetLastError();
 }

@@ -22,7 +22,11 @@
  *     of the last error on the calling thread is g3attn_last_error().  A
  *     device-side fault surfaces at the caller's next synchronisation.
  *   - GQA: query head h reads KV head h / (Hq / Hkv) (contiguous groups).
- *   - Supported now: D = 128, Hq / Hkv in {1, 2, 4, 8}.
+ *   - Supported: D = 128 (the 27B print's q/k norms are over 128 values)
+ *     and D = 256 (the 1B print: q_proj 1152 -> 1024 = 4 heads x 256,
+ *     k_proj/v_proj 1152 -> 256 = 1 KV head, norms over 256 values; both in
+ *     "Gemma explained: What's new in Gemma 3", model prints); Hq / Hkv in
+ *     {1, 2, 4, 8}.
  */
 #ifndef G3ATTN_H
 #define G3ATTN_H
@@ -41,7 +45,7 @@ enum { G3_LOCAL = 0, G3_GLOBAL = 1 };
 enum {
   G3_OK = 0,
   G3_EINVAL = -1,       /* bad argument (shape, pointer, alignment, range) */
-  G3_EUNSUPPORTED = -2, /* valid but not implemented (e.g. D != 128) */
+  G3_EUNSUPPORTED = -2, /* valid but not implemented (e.g. D not 128 or 256) */
   G3_EHIP = -3,         /* a HIP launch failed */
   G3_EWORKSPACE = -4    /* workspace missing or too small */
 };

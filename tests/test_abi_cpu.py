@@ -42,6 +42,13 @@ def test_workspace_sizes(L):
     # fewer pairs: the ring splits 4 ways (256 slots each)
     assert L.g3attn_decode_workspace_size(2, 32, 16, 128, 32768, ctypes.byref(ring)) == 2 * 32 * 4 * 130 * 4
     assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(lin)) == 32 * 32 * 9 * 130 * 4
+    # head dim 256 (Gemma 3 1B: 4 query heads, 1 kv head): keys [1][1][4096][256] bf16, then 8 flags per
+    # 128-position tile of G = 1 (the most work items any group size gives)
+    assert L.g3attn_prefill_workspace_size(1, 4096, 4, 1, 256) == 4096 * 256 * 2 + 32 * 8 * 4
+    # 4 sequence x kv-head pairs over 128 units of 256 slots: too few pairs for longer splits -> 128 splits
+    assert L.g3attn_decode_workspace_size(4, 4, 1, 256, 32767, ctypes.byref(G.KVCacheC(0, 0, 32768, 0))) == \
+        4 * 4 * 128 * 258 * 4
+    assert L.g3attn_decode_workspace_size(1, 4, 1, 64, 100, ctypes.byref(ring)) == 0
 
 
 FAKE = 1 << 20  # a 16-byte aligned non-null address: validation fails before any use
@@ -105,7 +112,7 @@ def test_decode_validation_errors(L):
         return L.g3attn_decode(FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"], a["D"], a["positions"], a["maxp"],
                                a["cache"], a["kind"], a["window"], 1e4, 1.0, None, None, 1e-6, 0.0, FAKE,
                                a["ws_bytes"], None)
-    assert dec(D=256) == G.G3_EUNSUPPORTED
+    assert dec(D=64) == G.G3_EUNSUPPORTED and "D=64" in _err(L)
     assert dec(B=0) == G.G3_EINVAL
     assert dec(cache=None) == G.G3_EINVAL
     assert dec(positions=None) == G.G3_EINVAL
