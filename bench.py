@@ -9,7 +9,10 @@ One step = one pass of the whole hot path over one batch of synthetic input:
                    layers, the full cache for the global one);
   * chunked leg  : a 4096-query chunk at positions 126976..131071 against a
                    131072-position cache (global, RoPE base 1e6 with position
-                   interpolation 8) plus the five local layers.
+                   interpolation 8) plus the five local layers;
+  * prefill_1b and decode_1b : the same two blocks at Gemma 3 1B shapes
+                   (Hq=4, Hkv=1, D=256): one 32768-token sequence, and 32
+                   sequences with 32767 cached positions.
 Beside the steps, once: the whole 62-layer 27B attention stack (52 local,
 10 global) over one 128K sequence, the prompt through chunked prefills of
 4096 tokens and then a decode loop, on per-layer caches (``schedule``).
@@ -44,7 +47,7 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,chunked")
+    ap.add_argument("--legs", default="prefill,decode,chunked,prefill_1b,decode_1b")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle-on-host baseline")
     ap.add_argument("--no-schedule", action="store_true", help="skip the 62-layer 128K schedule run")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -73,20 +76,21 @@ def _events(torch, n):
     return evs
 
 
-def build_prefill_leg(torch, G, W, C):
-    w = W.WORKLOADS[2]
-    leg = Leg("prefill")
+def build_prefill_leg(torch, G, W, C, cfg=2, name="prefill"):
+    w = W.WORKLOADS[cfg]
+    c = w.config
+    leg = Leg(name)
     leg.unit = "flop"
     leg.workload = w
     leg.inputs = []
     for l in range(LAYERS):
         kind = G.layer_kind(l)
         base = W.ROPE_BASE_GLOBAL if kind == G.GLOBAL else W.ROPE_BASE_LOCAL
-        q = W.device_normal_bf16((w.B, w.S, w.Hq, w.D), W.seed_of(2, l, W.T_Q))
-        k = W.device_normal_bf16((w.B, w.S, w.Hkv, w.D), W.seed_of(2, l, W.T_K))
-        v = W.device_normal_bf16((w.B, w.S, w.Hkv, w.D), W.seed_of(2, l, W.T_V))
-        gq = torch.from_numpy(W.host_gamma(w.D, W.seed_of(2, l, W.T_GQ))).cuda()
-        gk = torch.from_numpy(W.host_gamma(w.D, W.seed_of(2, l, W.T_GK))).cuda()
+        q = W.device_normal_bf16((w.B, w.S, w.Hq, w.D), W.seed_of(c, l, W.T_Q))
+        k = W.device_normal_bf16((w.B, w.S, w.Hkv, w.D), W.seed_of(c, l, W.T_K))
+        v = W.device_normal_bf16((w.B, w.S, w.Hkv, w.D), W.seed_of(c, l, W.T_V))
+        gq = torch.from_numpy(W.host_gamma(w.D, W.seed_of(c, l, W.T_GQ))).cuda()
+        gk = torch.from_numpy(W.host_gamma(w.D, W.seed_of(c, l, W.T_GK))).cuda()
         o = torch.empty_like(q)
         ws = torch.empty(G.prefill_workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device="cuda")
         leg.inputs.append((q, k, v, gq, gk, kind))
@@ -98,9 +102,10 @@ def build_prefill_leg(torch, G, W, C):
     return leg
 
 
-def build_decode_leg(torch, G, W, C):
-    w = W.WORKLOADS[3]
-    leg = Leg("decode")
+def build_decode_leg(torch, G, W, C, cfg=3, name="decode"):
+    w = W.WORKLOADS[cfg]
+    c = w.config
+    leg = Leg(name)
     leg.unit = "byte"
     leg.workload = w
     p = w.pos0
@@ -109,14 +114,14 @@ def build_decode_leg(torch, G, W, C):
         kind = G.layer_kind(l)
         base = W.ROPE_BASE_GLOBAL if kind == G.GLOBAL else W.ROPE_BASE_LOCAL
         cap = W.RING_CAP if kind == G.LOCAL else p + 64  # global: positions 0..p (p+1 slots), padded
-        ck = W.device_normal_bf16((w.B, w.Hkv, cap, w.D), W.seed_of(3, l, W.T_CK))
-        cv = W.device_normal_bf16((w.B, w.Hkv, cap, w.D), W.seed_of(3, l, W.T_CV))
+        ck = W.device_normal_bf16((w.B, w.Hkv, cap, w.D), W.seed_of(c, l, W.T_CK))
+        cv = W.device_normal_bf16((w.B, w.Hkv, cap, w.D), W.seed_of(c, l, W.T_CV))
         cache = G.KVCache(ck, cv, is_ring=(kind == G.LOCAL))
-        q = W.device_normal_bf16((w.B, w.Hq, w.D), W.seed_of(3, l, W.T_Q))
-        kn = W.device_normal_bf16((w.B, w.Hkv, w.D), W.seed_of(3, l, W.T_K))
-        vn = W.device_normal_bf16((w.B, w.Hkv, w.D), W.seed_of(3, l, W.T_V))
-        gq = torch.from_numpy(W.host_gamma(w.D, W.seed_of(3, l, W.T_GQ))).cuda()
-        gk = torch.from_numpy(W.host_gamma(w.D, W.seed_of(3, l, W.T_GK))).cuda()
+        q = W.device_normal_bf16((w.B, w.Hq, w.D), W.seed_of(c, l, W.T_Q))
+        kn = W.device_normal_bf16((w.B, w.Hkv, w.D), W.seed_of(c, l, W.T_K))
+        vn = W.device_normal_bf16((w.B, w.Hkv, w.D), W.seed_of(c, l, W.T_V))
+        gq = torch.from_numpy(W.host_gamma(w.D, W.seed_of(c, l, W.T_GQ))).cuda()
+        gk = torch.from_numpy(W.host_gamma(w.D, W.seed_of(c, l, W.T_GK))).cuda()
         o = torch.empty_like(q)
         ws = torch.empty(G.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, p, cache), dtype=torch.uint8, device="cuda")
 
@@ -283,6 +288,10 @@ def _src_hash(name):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
+def _model_tag(w):
+    return "1b" if w.D == 256 else "27b"
+
+
 def _traffic(kernel_src, launches_key):
     """Measured HBM bytes per launch from the committed counter summary, if
     it was taken on the current kernel source; else None."""
@@ -314,7 +323,9 @@ def main():
     torch.cuda.set_device(0)
     legs = []
     names = [s for s in args.legs.split(",") if s]
-    builders = {"prefill": build_prefill_leg, "decode": build_decode_leg, "chunked": build_chunked_leg}
+    builders = {"prefill": build_prefill_leg, "decode": build_decode_leg, "chunked": build_chunked_leg,
+                "prefill_1b": lambda *a: build_prefill_leg(*a, cfg=9, name="prefill_1b"),
+                "decode_1b": lambda *a: build_decode_leg(*a, cfg=10, name="decode_1b")}
     for n in names:
         leg = builders[n](torch, G, W, C)
         leg.ev_leg = _events(torch, 1)[0]
@@ -365,36 +376,42 @@ def main():
            "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, random-init, in HBM)"}
     by = {leg.name: leg for leg in legs}
-    if "prefill" in by:
-        leg = by["prefill"]
+
+    def prefill_summary(leg):
         w = leg.workload
-        ms = leg_ms["prefill"] / K
+        ms = leg_ms[leg.name] / K
         flops = sum(leg.work)
-        out["value"] = flops / (ms * 1e-3) / 1e12
-        kms = [x / KK for x in main_ms["prefill"]]
+        kms = [x / KK for x in main_ms[leg.name]]
         achieved = flops / (sum(kms) * 1e-3) / 1e12
-        out["config"] = {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
-                         "layers": "LLLLLG", "window": W.WINDOW, "rope_base": [W.ROPE_BASE_LOCAL, W.ROPE_BASE_GLOBAL],
-                         "in_window_flop_per_block": flops, "prefill_block_ms": ms}
-        out["roofline"] = {"bound": "mfma", "kernel": "prefill_fwd", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                           "traffic": _traffic("prefill.hip", "prefill_fwd_27b_block"),
-                           "launch_ms": kms, "launch_flop": leg.work}
-    if "decode" in by:
-        leg = by["decode"]
+        cfg = {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "layers": "LLLLLG",
+               "window": W.WINDOW, "rope_base": [W.ROPE_BASE_LOCAL, W.ROPE_BASE_GLOBAL],
+               "in_window_flop_per_block": flops, "prefill_block_ms": ms}
+        kern = "prefill_fwd" if w.D == 128 else "prefill_fwd_d256"
+        src = "prefill.hip" if w.D == 128 else "prefill_d256.hip"
+        roof = {"bound": "mfma", "kernel": kern, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": _traffic(src, f"{kern}_{_model_tag(w)}_block"),
+                "launch_ms": kms, "launch_flop": leg.work}
+        return flops / (ms * 1e-3) / 1e12, cfg, roof
+
+    def decode_summary(leg):
         w = leg.workload
-        ms = leg_ms["decode"] / K
+        ms = leg_ms[leg.name] / K
         nbytes = sum(leg.work)
-        kms = [x / KK for x in main_ms["decode"]]
+        kms = [x / KK for x in main_ms[leg.name]]
         # split-K kernel: KV bytes only (q/o/new rows are handled around it)
         kv_bytes = [b - 2.0 * w.D * (2 * w.B * w.Hq + 2 * w.B * w.Hkv) for b in leg.work]
         ach = sum(kv_bytes) / (sum(kms) * 1e-3) / 1e9
-        out["decode"] = {"value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "workload": w.name, "ms": ms,
-                         "bytes_per_block": nbytes, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                         "roofline": {"bound": "hbm", "kernel": "decode_splitk", "achieved": ach,
-                                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS,
-                                      "traffic": _traffic("decode.hip", "decode_splitk_27b_block"),
-                                      "launch_ms": kms}}
+        return {"value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "workload": w.name, "ms": ms,
+                "bytes_per_block": nbytes, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                "roofline": {"bound": "hbm", "kernel": "decode_splitk", "achieved": ach, "peak": PEAK_HBM_GBPS,
+                             "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS,
+                             "traffic": _traffic("decode.hip", f"decode_splitk_{_model_tag(w)}_block"),
+                             "launch_ms": kms}}
+
+    if "prefill" in by:
+        out["value"], out["config"], out["roofline"] = prefill_summary(by["prefill"])
+    if "decode" in by:
+        out["decode"] = decode_summary(by["decode"])
     if "chunked" in by:
         leg = by["chunked"]
         ms = leg_ms["chunked"] / K
@@ -403,6 +420,14 @@ def main():
         out["chunked_prefill"] = {"value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
                                   "workload": leg.workload.name, "ms": ms, "in_window_flop_per_block": flops,
                                   "kernel_TFLOPs": flops / (sum(kms) * 1e-3) / 1e12, "launch_ms": kms}
+    if "prefill_1b" in by or "decode_1b" in by:
+        g1 = {}
+        if "prefill_1b" in by:
+            v, cfg, roof = prefill_summary(by["prefill_1b"])
+            g1["prefill"] = {"value": v, "unit": "TFLOP/s", "config": cfg, "roofline": roof}
+        if "decode_1b" in by:
+            g1["decode"] = decode_summary(by["decode_1b"])
+        out["gemma3_1b"] = g1
     if out["value"] is None:
         out["value"] = 0.0
     if not args.no_schedule:

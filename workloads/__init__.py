@@ -17,9 +17,11 @@ Recipe (used everywhere):
     back from the device.
 
 Shapes follow the 27B module print on "Gemma explained: What's new in
-Gemma 3" (32 query heads, 16 KV heads, head_dim 128), the 1024-token local
-span and 128K context of the Technical Report (sections 1 and 2), and the
-256-token image size (Technical Report, section 1).
+Gemma 3" (32 query heads, 16 KV heads, head_dim 128) and, for the 1B
+workloads, that page's 1B print (4 query heads, 1 KV head, head_dim 256),
+the 1024-token local span and the 128K (1B: 32K) context of the Technical
+Report (sections 1 and 2), and the 256-token image size (Technical Report,
+section 1).
 """
 from __future__ import annotations
 
@@ -108,7 +110,8 @@ class Workload:
     max_spans: int = 0
 
 
-# The five workloads (shapes from the 27B module print; see module docstring).
+# The five 27B-shaped workloads (shapes from the 27B module print; see the
+# module docstring) and two of the 1B model.
 WORKLOADS = {
     1: Workload(1, "single-layer-2k", B=1, S=2048, Hq=4, Hkv=2, D=128, kinds=("local", "global")),
     2: Workload(2, "27b-prefill-8k-block", B=1, S=8192, Hq=32, Hkv=16, D=128,
@@ -120,6 +123,12 @@ WORKLOADS = {
                 pos0=126976, cached=126976, mode="chunked"),
     5: Workload(5, "mixed-mask-4k", B=2, S=4096, Hq=16, Hkv=8, D=128, kinds=("local", "global"),
                 max_spans=4),
+    # Gemma 3 1B shapes (1B module print: 4 query heads, 1 KV head,
+    # head_dim 256) at its 32K context (Technical Report, section 2).
+    9: Workload(9, "1b-prefill-32k-block", B=1, S=32768, Hq=4, Hkv=1, D=256,
+                kinds=("local",) * 5 + ("global",)),
+    10: Workload(10, "1b-decode-32k-block", B=32, S=1, Hq=4, Hkv=1, D=256,
+                 kinds=("local",) * 5 + ("global",), pos0=32767, cached=32767, mode="decode"),
 }
 
 
