@@ -88,7 +88,7 @@ hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStr
 constexpr int kPrefillWaves = G3_PREFILL_WAVES;
 // Tiles: positions per prefill workgroup for a GQA group of size G.
 inline int prefill_rows_per_wg(int G) { return kPrefillWaves * (32 / G); }
-constexpr int kPrefillWavesD256 = 4;
+constexpr int kPrefillWavesD256 = 8;
 inline int prefill_rows_per_wg_d256(int G) { return kPrefillWavesD256 * (32 / G); }
 
 }  // namespace g3

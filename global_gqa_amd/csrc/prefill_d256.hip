@@ -6,19 +6,26 @@
 // visible = causal j <= i or the same image span, and |i - j| < window on
 // local layers (Gemma 3 Technical Report, sections 1-2).
 //
-// Design (workgroup = 4 waves, one per SIMD, one (sequence, kv head, query
+// Design (workgroup = 8 waves, two per SIMD, one (sequence, kv head, query
 // tile)):
 //   * each wave owns 32 query rows = (32/G positions) x (G heads of one kv
 //     group); Q^ (QK-RMSNorm, RoPE, scale in log2 units) stays in registers
 //     as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16, 16 dim
 //     steps); P^T goes from the S^T accumulators into the B operand of
 //     O^T = V^T P^T (8 blocks of 32 dims), V^T through transposing LDS reads;
-//   * K/V tiles of 32 keys x 512 B, double-buffered in LDS and filled by
-//     global->LDS loads, chunk c of row r at chunk position c ^ swz(r mod 16)
-//     (bank groups repeat every 256 B, so the D = 128 kernel's conflict-free
-//     read patterns carry over);
-//   * one wave per SIMD with the whole register file: O (128 registers), Q
-//     (64) and a whole tile's operands in flight;
+//   * ping-pong: the two waves of a SIMD (w, w + 4) alternate halves of every
+//     32-key tile, one running its 32 MFMAs (PV of the previous tile, then QK
+//     of this one) while the other runs its softmax and its share of the tile
+//     loads, so that the MFMA pipe and the VALU work side by side (a wave's
+//     own VALU work does not overlap its MFMAs);
+//   * O (128 registers) and Q (64) fill most of the 256 registers a wave has
+//     at two waves per SIMD, so the matrix half computes no addresses: K and V
+//     rows sit in LDS with padded strides (K 528 B, V 576 B; conflict-free for
+//     ds_read_b128 and for the transposing reads respectively) and every
+//     operand read is one base register plus an immediate offset;
+//   * K/V tiles of 32 keys in a ring of 4 LDS slots, filled by global->LDS
+//     loads whose lanes each fetch the 16-byte piece their slot position holds
+//     (pad positions read a zero row);
 //   * softmax without a running maximum (QK-RMSNorm bounds the logits), with
 //     the same flagged second pass (ONLINE = true) as the D = 128 kernel.
 #include "g3_common.hpp"
@@ -30,10 +37,22 @@ namespace {
 
 constexpr int kDh = 256;             // head dimension
 constexpr int kBNh = 32;             // keys per tile
-constexpr int kTileH = kBNh * kDh;   // bf16 elements per tile (16 KiB)
 constexpr int kNW = kPrefillWavesD256;
+constexpr int kNB = 4;               // K/V tile slots in the LDS ring
+constexpr int kKRow = 33;            // K row stride in 16-byte pieces (528 B: 32 data + 1 pad)
+constexpr int kVRow = 36;            // V row stride in 16-byte pieces (576 B: 32 data + 4 pad)
+constexpr int kKLoads = 17;          // 1 KiB loads per K tile (33 * 32 = 1056 pieces, padded to 1088)
+constexpr int kVLoads = 18;          // 1 KiB loads per V tile (36 * 32 = 1152 pieces)
+constexpr int kKBytes = kKLoads * 1024;
+constexpr int kVBytes = kVLoads * 1024;
+constexpr int kSlotBytes = kKBytes + kVBytes;  // 35840
+constexpr int kLoads = kKLoads + kVLoads;      // 35 per tile: wave w issues loads w, w + 8, ...
+#ifndef G3_D256_AHEAD
+#define G3_D256_AHEAD 2
+#endif
+constexpr int kAhead = G3_D256_AHEAD;         // matrix-half operands read this many MFMAs ahead
 
-__device__ __forceinline__ int swz16(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+static_assert(kNW == 8, "two waves per SIMD");
 
 __device__ __forceinline__ float xhalf_sum256(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -48,6 +67,14 @@ __device__ __forceinline__ float xhalf_max256(float x) {
 // loads still in flight).
 __device__ __forceinline__ void barrier_lds256() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_loads256() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most one tile's loads of this wave (4 or 5) are in flight.
+__device__ __forceinline__ void wait_loads256_but(int n) {
+  if (n == 5)
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
+__device__ __forceinline__ void fence256() { __builtin_amdgcn_sched_barrier(0); }
 
 // One 16-byte global -> LDS load per lane: lane L writes LDS bytes
 // [lds_addr + 16 L, +16) (global_load_lds_dwordx4, address in M0, which is
@@ -63,11 +90,9 @@ __device__ __forceinline__ void dma16_256(const void* src, uint32_t lds_addr) {
       : "=&s"(saved)
       : "v"(src), "s"(lds_addr));
 }
-__device__ __forceinline__ uint32_t lds_addr256(const uint16_t* p) {
-  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)p);
-}
 
-// A zero K/V row: the source of tile rows whose key does not exist.
+// A zero K/V row: the source of tile rows whose key does not exist and of
+// pad positions.
 __device__ __attribute__((aligned(256))) uint16_t g_zero_row256[kDh] = {0};
 
 __device__ __forceinline__ int floor_div32(int x) { return x >= 0 ? x / 32 : -((31 - x) / 32); }
@@ -91,6 +116,10 @@ __device__ __forceinline__ Range256 row_range256(int i, int b, int kmin_avail, c
   return Range256{lo, hi};
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+
 }  // namespace
 
 template <int G, bool ONLINE>
@@ -98,9 +127,10 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
                                                                 RopeTable rt) {
   constexpr int P = 32 / G;    // positions per wave
   constexpr int WP = kNW * P;  // positions per workgroup
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * kTileH];  // K0 K1 V0 V1
-  auto lds_k = [&](int buf) { return lds + buf * kTileH; };
-  auto lds_v = [&](int buf) { return lds + (2 + buf) * kTileH; };
+  __shared__ __attribute__((aligned(1024))) char lds[kNB * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) float s_gamma[kDh];
+  lds_char* const ldsp = (lds_char*)lds;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)ldsp;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -115,11 +145,13 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   const int qt = a.n_qtiles - 1 - (li - bg * a.n_qtiles);  // heaviest tiles first
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
-  const int p0 = pos0_of(p0t, b);
+  // the per-sequence table is indexed at run time, which the compiler reads
+  // per lane: make the (uniform) result scalar, and everything derived from it
+  const int p0 = __builtin_amdgcn_readfirstlane(pos0_of(p0t, b));
   const int chunk_end = p0 + a.S;
   const int kmin_avail = a.has_cache ? (a.is_ring ? max(0, p0 - a.cap) : 0) : p0;
   const int qbase = p0 + qt * WP;
-  const int wbase = qbase + wave * P;
+  const int wbase = qbase + wave_u * P;  // wave-uniform: the key-range bounds below stay scalar
 
   // key tiles of the workgroup (lo(i), hi(i) are non-decreasing in i)
   const int wg_last = min(qbase + WP, chunk_end) - 1;
@@ -127,136 +159,157 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   const Range256 wl = row_range256(wg_last, b, kmin_avail, a, spt);
   const int t_begin = floor_div32(wf.lo - p0);
   const int n_t = floor_div32(wl.hi - p0) - t_begin + 1;
-  int w_lo_min = 0x7fffffff, w_hi_max = -0x7fffffff, w_lo_max = 0x7fffffff, w_hi_min = -0x7fffffff;
+  int w_lo_max = 0x7fffffff, w_hi_min = -0x7fffffff;
   if (wbase < chunk_end) {
-    const Range256 f = row_range256(wbase, b, kmin_avail, a, spt);
-    const Range256 l = row_range256(min(wbase + P, chunk_end) - 1, b, kmin_avail, a, spt);
-    w_lo_min = f.lo;
-    w_hi_min = f.hi;
-    w_lo_max = l.lo;
-    w_hi_max = l.hi;
+    w_hi_min = __builtin_amdgcn_readfirstlane(row_range256(wbase, b, kmin_avail, a, spt).hi);
+    w_lo_max = __builtin_amdgcn_readfirstlane(row_range256(min(wbase + P, chunk_end) - 1, b, kmin_avail, a, spt).lo);
   }
 
-  // ---- tile loader: wave w fills rows [8w, 8w + 8) of the K and V tiles, 2
-  // rows per instruction: lane L lands on row 8w + 2i + L/32, chunk position
-  // L % 32, so it fetches logical chunk (L % 32) ^ swz(row mod 16).
+  // ---- tile loader.  Load k (0..34) of a tile writes the 64 16-byte pieces
+  // [64 k', 64 k' + 64) of the slot's K region (k' = k < 17) or V region
+  // (k' = k - 17), piece n being (row n / stride, chunk n % stride); chunks
+  // past 32 and rows past 32 are padding.  Wave w issues loads w, w + 8, ...
   const uint16_t* khat_bg = a.khat + ((long long)b * a.Hkv + g) * a.S * kDh;
   const uint16_t* v_bg = a.v + ((long long)b * a.S * a.Hkv + g) * kDh;
   const int vstride = a.Hkv * kDh;
   const long long cache_bg = ((long long)b * a.Hkv + g) * (long long)a.cap * kDh;
-  auto dma_tile = [&](int t, int buf) {
+  const int n_my_loads = (kLoads - wave_u + kNW - 1) / kNW;  // 5 for waves 0-2, else 4
+  // the loader reads kernel-argument fields through locals (selecting
+  // between fields of the argument struct would keep it in scratch memory)
+  const int cap = a.cap, is_ring = a.is_ring, has_cache = a.has_cache;
+  const uint16_t* ck_bg = has_cache ? a.ck + cache_bg : nullptr;
+  const uint16_t* cv_bg = has_cache ? a.cv + cache_bg : nullptr;
+  auto dma_tile = [&](int t, int slot) {
     const int ts = p0 + t * kBNh;
     const int mode = (t >= 0 && ts + kBNh <= chunk_end) ? 0
-                     : (a.has_cache && ts >= kmin_avail && ts + kBNh <= p0 && (!a.is_ring || a.cap >= kBNh)) ? 1
+                     : (has_cache && ts >= kmin_avail && ts + kBNh <= p0 && (!is_ring || cap >= kBNh)) ? 1
                                                                                                       : 2;
-    const int slot0 = (mode == 1 && a.is_ring) ? ts % a.cap : ts;
+    const int slot0 = (mode == 1 && is_ring) ? ts % cap : ts;
+    // An opaque copy of the lane index: the per-lane piece coordinates are
+    // recomputed at every call instead of being kept in registers across the
+    // tile loop, where O and Q leave no room for them.
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int i = k & 3;
-      const bool is_v = k >= 4;
-      const int row = 8 * wave + 2 * i + (lane >> 5);
-      const int col = ((lane & 31) ^ swz16(row & 15)) * 8;
-      const uint16_t* src;
-      if (mode == 0) {
-        const int r = t * kBNh + row;
-        src = is_v ? v_bg + (long long)r * vstride : khat_bg + (long long)r * kDh;
-      } else if (mode == 1) {
-        int slot = slot0 + row;
-        if (a.is_ring && slot >= a.cap) slot -= a.cap;
-        src = (is_v ? a.cv : a.ck) + cache_bg + (long long)slot * kDh;
-      } else {
-        const int j = ts + row;
-        src = g_zero_row256;
-        if (j >= p0 && j < chunk_end) {
-          src = is_v ? v_bg + (long long)(j - p0) * vstride : khat_bg + (long long)(j - p0) * kDh;
-        } else if (a.has_cache && j < p0 && j >= kmin_avail) {
-          const long long slot = a.is_ring ? (long long)(j % a.cap) : (long long)j;
-          src = (is_v ? a.cv : a.ck) + cache_bg + slot * kDh;
+    for (int j = 0; j < 5; ++j) {
+      const int k = wave_u + kNW * j;
+      if (k < kLoads) {
+        const bool is_v = k >= kKLoads;
+        const int kk = is_v ? k - kKLoads : k;
+        const int n = 64 * kk + lane_o;
+        const int row = is_v ? n / kVRow : n / kKRow;
+        const int col = is_v ? n - row * kVRow : n - row * kKRow;
+        const bool data = row < kBNh && col < 32;
+        // pad positions are never read: in the uniform modes they fetch the
+        // tile's first piece, which exists
+        const int rr = data ? row : 0;
+        const int cc = data ? col : 0;
+        const uint16_t* src;
+        if (mode == 0) {
+          const uint16_t* base = is_v ? v_bg + (long long)t * kBNh * vstride : khat_bg + (long long)t * kBNh * kDh;
+          src = base + (uint32_t)(rr * (is_v ? vstride : kDh) + 8 * cc);
+        } else if (mode == 1 && (!is_ring || slot0 + kBNh <= cap)) {
+          const uint16_t* base = (is_v ? cv_bg : ck_bg) + (long long)slot0 * kDh;
+          src = base + (uint32_t)(rr * kDh + 8 * cc);
+        } else if (mode == 1) {
+          int sl = slot0 + rr;
+          if (sl >= cap) sl -= cap;
+          src = (is_v ? cv_bg : ck_bg) + (long long)sl * kDh + 8 * cc;
+        } else {
+          const int jj = ts + row;
+          src = g_zero_row256;
+          if (data) {
+            if (jj >= p0 && jj < chunk_end) {
+              src = (is_v ? v_bg + (long long)(jj - p0) * vstride : khat_bg + (long long)(jj - p0) * kDh) + 8 * col;
+            } else if (has_cache && jj < p0 && jj >= kmin_avail) {
+              const long long sl = is_ring ? (long long)(jj % cap) : (long long)jj;
+              src = (is_v ? cv_bg : ck_bg) + sl * kDh + 8 * col;
+            }
+          }
         }
+        dma16_256(src, lds0 + slot * kSlotBytes + (is_v ? kKBytes : 0) + 1024 * kk);
       }
-      const uint16_t* dst = (is_v ? lds_v(buf) : lds_k(buf)) + (8 * wave_u + 2 * i) * kDh;
-      dma16_256(src + col, lds_addr256(dst));
     }
   };
 
-  // operand read offsets inside a tile (bytes)
-  uint32_t adk[16];     // K^T step st: row ln, chunk (2 st + h2)
-  uint32_t adv[2][8];   // V^T [row half][dim block]: transposing reads
-#pragma unroll
-  for (int st = 0; st < 16; ++st) adk[st] = ln * 512 + (((2 * st + h2) ^ swz16(ln & 15)) << 4);
-  {
-    const int g4 = lane >> 4, w16 = lane & 15;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const int row = 8 * hf + 4 * (g4 >> 1) + (w16 >> 2);
-        const int c = 4 * mb + 2 * (g4 & 1) + ((w16 & 3) >> 1);
-        adv[hf][mb] = row * 512 + ((c ^ swz16(row)) << 4) + 8 * (w16 & 1);
-      }
-  }
+  for (int k = 0; k < 2 && k < n_t; ++k) dma_tile(t_begin + k, k);
+  // slot 3's V region reads as zeros: the first tile's "previous tile" PV
+  // (with P = 0) runs on it
+  for (int n = tid; n < kVBytes / 16; n += 64 * kNW)
+    *(__attribute__((address_space(3))) u32x4*)(ldsp + (kNB - 1) * kSlotBytes + kKBytes + 16 * n) =
+        u32x4{0, 0, 0, 0};
 
-  dma_tile(t_begin, 0);
-
+  // Values derived from the lane index are recomputed where they are used
+  // (from an opaque copy of the index) instead of being kept in registers
+  // across the tile loop, where O and Q leave no room for them.
+  auto lane_opaque = [&]() {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
   // this lane's query row: position offset ln % P, head ln / P of the group
   const int hg = ln / P;
   const int row_pos = wbase + (ln - hg * P);
   const bool row_ok = row_pos < chunk_end;
-  int row_lo = 0x7fffffff, row_hi = -0x7fffffff;
-  if (row_ok) {
-    const Range256 rr = row_range256(row_pos, b, kmin_avail, a, spt);
-    row_lo = rr.lo;
-    row_hi = rr.hi;
-  }
 
   // ---- Q prologue: QK-RMSNorm, RoPE, scale * log2(e), bf16: lane (ln, h2)
   // holds dims 16 s + 8 h2 + [0, 8) of row ln, s = 0..15; the rotation pairs
-  // (d, d + 128) are s and s + 8 of the same lane.
+  // (d, d + 128) are s and s + 8 of the same lane.  Q stays packed (64
+  // registers) and is rotated one pair of 8-dim pieces at a time, with q_gamma
+  // staged in LDS, to keep the prologue within the registers O and Q leave.
   bf16x8 qreg[16];
   {
     const int r = row_ok ? row_pos - p0 : 0;  // valid address; rows past the end are never stored
     const uint16_t* src = a.q + (((long long)b * a.S + r) * a.Hq + g * G + hg) * kDh + 8 * h2;
-    float x[128];
+    u32x4 w[16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const u32x4 w = *(const u32x4*)(src + 16 * s);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[8 * s + 2 * e] = bf_lo(w[e]);
-        x[8 * s + 2 * e + 1] = bf_hi(w[e]);
-      }
-    }
+    for (int s = 0; s < 16; ++s) w[s] = *(const u32x4*)(src + 16 * s);
+    if (a.q_gamma && wave_u == 0) dma16_256(a.q_gamma + 4 * lane, (uint32_t)(uintptr_t)(lds_char*)s_gamma);
+    wait_loads256();
+    barrier_lds256();  // tiles 0 and 1, the zero V region and q_gamma are in LDS
     float rn = a.sl2;
     if (a.q_gamma) {
       float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < 128; ++e) ss += x[e] * x[e];
-      ss = xhalf_sum256(ss);
-      rn *= rsqrtf(ss * (1.f / kDh) + a.eps);
-#pragma unroll
       for (int s = 0; s < 16; ++s)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[8 * s + e] *= a.q_gamma[16 * s + 8 * h2 + e];
+        for (int e = 0; e < 4; ++e) ss += bf_lo(w[s][e]) * bf_lo(w[s][e]) + bf_hi(w[s][e]) * bf_hi(w[s][e]);
+      ss = xhalf_sum256(ss);
+      rn *= rsqrtf(ss * (1.f / kDh) + a.eps);
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < 8; ++s) {
+      float x1[8], x2[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float sn, cs;
-        rope_sincos(row_pos, rt.rev[16 * s + 8 * h2 + e], sn, cs);
-        const float x1 = x[8 * s + e] * rn, x2 = x[8 * (s + 8) + e] * rn;
-        x[8 * s + e] = x1 * cs - x2 * sn;
-        x[8 * (s + 8) + e] = x1 * sn + x2 * cs;
+      for (int e = 0; e < 4; ++e) {
+        x1[2 * e] = bf_lo(w[s][e]) * rn;
+        x1[2 * e + 1] = bf_hi(w[s][e]) * rn;
+        x2[2 * e] = bf_lo(w[s + 8][e]) * rn;
+        x2[2 * e + 1] = bf_hi(w[s + 8][e]) * rn;
       }
+      if (a.q_gamma) {
+        lds_f32x4* g1 = (lds_f32x4*)((lds_char*)s_gamma + 4 * (16 * s + 8 * h2));
+        lds_f32x4* g2 = (lds_f32x4*)((lds_char*)s_gamma + 4 * (16 * (s + 8) + 8 * h2));
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      u32x4 w = {pack2(x[8 * s], x[8 * s + 1]), pack2(x[8 * s + 2], x[8 * s + 3]), pack2(x[8 * s + 4], x[8 * s + 5]),
-                 pack2(x[8 * s + 6], x[8 * s + 7])};
-      qreg[s] = __builtin_bit_cast(bf16x8, w);
+        for (int e = 0; e < 8; ++e) {
+          x1[e] *= g1[e >> 2][e & 3];
+          x2[e] *= g2[e >> 2][e & 3];
+        }
+      }
+      uint32_t y1[4], y2[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float sn0, cs0, sn1, cs1;
+        rope_sincos(row_pos, rt.rev[16 * s + 8 * h2 + e], sn0, cs0);
+        rope_sincos(row_pos, rt.rev[16 * s + 8 * h2 + e + 1], sn1, cs1);
+        y1[e >> 1] = pack2(x1[e] * cs0 - x2[e] * sn0, x1[e + 1] * cs1 - x2[e + 1] * sn1);
+        y2[e >> 1] = pack2(x1[e] * sn0 + x2[e] * cs0, x1[e + 1] * sn1 + x2[e + 1] * cs1);
+      }
+      qreg[s] = __builtin_bit_cast(bf16x8, u32x4{y1[0], y1[1], y1[2], y1[3]});
+      qreg[s + 8] = __builtin_bit_cast(bf16x8, u32x4{y2[0], y2[1], y2[2], y2[3]});
+      fence256();
     }
   }
-  wait_loads256();
-  barrier_lds256();  // the first tile is in LDS
 
   f32x16 o[8];
 #pragma unroll
@@ -267,91 +320,172 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   float m_run = -__builtin_huge_valf();
   const float NEG_INF = -__builtin_huge_valf();
 
-  for (int it = 0; it < n_t; ++it) {
-    const int t = t_begin + it;
-    const int buf = it & 1;
-    // Tile t+1 goes to the other buffer: every wave finished reading it
-    // (tile t-1) before the previous barrier.
-    if (it + 1 < n_t) dma_tile(t + 1, buf ^ 1);
-    const int ts = p0 + t * kBNh;
-    const bool act = ts <= w_hi_max && ts + kBNh - 1 >= w_lo_min;
-    if (act) {
-      const bool full = ts >= w_lo_max && ts + kBNh - 1 <= w_hi_min;
-      const char* kl = (const char*)lds_k(buf);
-      const char* vl = (const char*)lds_v(buf);
-      // S^T (32 keys x 32 queries) = K Q^T over 16 dim steps
-      bf16x8 kop[16];
+  // operand bases inside slot 0 (bytes).  K step st of row ln: piece
+  // 2 st + h2 of row ln; V^T (transposing reads): rows 4 (g4 / 2) + w16 / 4
+  // (+8 for the second read, +16 for the second 16-key half), piece
+  // 4 mb + 2 (g4 & 1) + (w16 & 3) / 2, byte 8 (w16 & 1).
+  auto operand_bases = [&](uint32_t& kbase, uint32_t& vbase) {
+    const int l = lane_opaque();
+    kbase = lds0 + (l & 31) * (16 * kKRow) + 16 * (l >> 5);
+    const int g4 = l >> 4, w16 = l & 15;
+    vbase = lds0 + kKBytes + (4 * (g4 >> 1) + (w16 >> 2)) * (16 * kVRow) + 16 * (2 * (g4 & 1) + ((w16 & 3) >> 1)) +
+            8 * (w16 & 1);
+  };
+  auto rd_k = [&](uint32_t kb, int st) -> bf16x8 {
+    return *(lds_bf16x8*)((lds_char*)(uintptr_t)kb + 32 * st);
+  };
+  auto rd_v = [&](uint32_t vb, int k) -> bf16x8 {
+    const int t2 = k >> 3, mb = k & 7;
+    lds_char* p = (lds_char*)(uintptr_t)vb + 16 * 16 * kVRow * t2 + 64 * mb;
+    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * 16 * kVRow));
+    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  // Matrix half: PV of the tile in slot vs (o[mb] += V^T P^T, 16 MFMAs),
+  // then, if DO_QK, S^T of the tile in slot ks (16 MFMAs).  Operands are
+  // read two MFMAs ahead through a 3-register rotation.
+  auto mfma_half = [&](auto do_qk_tag, int vs, int ks, const bf16x8 (&pb)[2], f32x16& s) {
+    constexpr bool DO_QK = decltype(do_qk_tag)::value;
+    constexpr int NM = DO_QK ? 32 : 16;
+    uint32_t kbase, vbase;
+    operand_bases(kbase, vbase);
+    const uint32_t vb = vbase + vs * kSlotBytes;
+    const uint32_t kb = kbase + ks * kSlotBytes;
+    bf16x8 op[kAhead + 1];
+    auto rd = [&](int k) { return k < 16 ? rd_v(vb, k) : rd_k(kb, k - 16); };
 #pragma unroll
-      for (int st = 0; st < 16; ++st) kop[st] = *(const bf16x8*)(kl + adk[st]);
-      f32x16 s = {};
+    for (int k = 0; k < kAhead; ++k) op[k] = rd(k);
+    fence256();
 #pragma unroll
-      for (int st = 0; st < 16; ++st) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[st], qreg[st], s, 0, 0, 0);
-      // V^T operands of the whole tile, read while the scores are computed
-      bf16x8 vop[2][8];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-          const char* base = vl + 8192 * t2;
-          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + adv[0][mb]));
-          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + adv[1][mb]));
-          vop[t2][mb] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      // softmax: key of register r = ts + 8 (r / 4) + 4 h2 + r % 4
-      if (!full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = ts + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if (j < row_lo || j > row_hi) s[r] = NEG_INF;
-        }
-      }
-      float off = 0.f;
-      if (ONLINE) {
-        float mx = NEG_INF;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = xhalf_max256(mx);
-        const float m_new = fmaxf(m_run, mx);
-        off = (m_new == NEG_INF) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - off);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
-      }
-      bf16x8 pb[2];
-      float rs = 0.f;
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        float e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          e[i] = fast_exp2(ONLINE ? s[8 * t2 + i] - off : s[8 * t2 + i]);
-          rs += e[i];
-        }
-        u32x4 u = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
-        pb[t2] = __builtin_bit_cast(bf16x8, u);
-      }
-      l_run += rs;
-      // O^T (256 dims x 32 queries) += V^T P^T
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t2][mb], pb[t2], o[mb], 0, 0, 0);
+    for (int k = 0; k < NM; ++k) {
+      if (k < 16)
+        o[k & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[k % (kAhead + 1)], pb[k >> 3], o[k & 7], 0, 0, 0);
+      else
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[k % (kAhead + 1)], qreg[k - 16], k == 16 ? f32x16{} : s, 0,
+                                                    0, 0);
+      if (k + kAhead < NM) op[(k + kAhead) % (kAhead + 1)] = rd(k + kAhead);
+      fence256();
     }
-    wait_loads256();
-    barrier_lds256();  // tile t+1 landed; every wave is past tile t's reads
-  }
+  };
+
+  // Softmax of S^T for the tile starting at key ts: p = exp2(s) (masked
+  // outside each row's range unless the tile is inside every row's range),
+  // packed to the PV operand; key of register r = ts + 8 (r / 4) + 4 h2 + r % 4.
+  auto softmax = [&](f32x16& s, int ts, bool full, bf16x8 (&pb)[2]) {
+    if (!full) {
+      const int l = lane_opaque();
+      const int lnl = l & 31, h2l = l >> 5;
+      const int rp = wbase + lnl % P;
+      int row_lo = 0x7fffffff, row_hi = -0x7fffffff;
+      if (rp < chunk_end) {
+        const Range256 rr = row_range256(rp, b, kmin_avail, a, spt);
+        row_lo = rr.lo;
+        row_hi = rr.hi;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = ts + 8 * (r >> 2) + 4 * h2l + (r & 3);
+        if (j < row_lo || j > row_hi) s[r] = NEG_INF;
+      }
+    }
+    float off = 0.f;
+    if (ONLINE) {
+      float mx = NEG_INF;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = xhalf_max256(mx);
+      const float m_new = fmaxf(m_run, mx);
+      off = (m_new == NEG_INF) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - off);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e[i] = fast_exp2(ONLINE ? s[8 * t2 + i] - off : s[8 * t2 + i]);
+        rs += e[i];
+      }
+      u32x4 u = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+      pb[t2] = __builtin_bit_cast(bf16x8, u);
+    }
+    l_run += rs;
+  };
+
+  // Ping-pong over the tiles (tile it in slot it % 4; the loads of tile
+  // it + 2 go to the slot of tile it - 2, free once both groups are past its
+  // PV).  Every tile takes two halves separated by workgroup barriers:
+  //   group A (waves 0-3): half 1 PV(it-1) + QK(it), half 2 softmax(it)
+  //   group B (waves 4-7): half 1 softmax(it-1),     half 2 PV(it-1) + QK(it)
+  // Before the closing barrier of tile it, tile it+1 must have landed.
+  // PV(-1) runs with P = 0 on the zeroed V region of slot 3.
+  auto run = [&](auto grp_b_tag) {
+    constexpr bool GB = decltype(grp_b_tag)::value;
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = NEG_INF;
+    bf16x8 pb[2];
+    pb[0] = pb[1] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    int s_ts = 0;
+    bool s_full = true;
+    for (int it = 0; it < n_t; ++it) {
+      const int t = t_begin + it;
+      const int ts = p0 + t * kBNh;
+      const bool full = ts >= w_lo_max && ts + kBNh - 1 <= w_hi_min;
+      const bool fetch = it + 2 < n_t;
+      const int vs = (it + kNB - 1) & (kNB - 1);
+      const int ks = it & (kNB - 1);
+      if (!GB) {
+        __builtin_amdgcn_s_setprio(1);
+        mfma_half(std::true_type{}, vs, ks, pb, s);
+        __builtin_amdgcn_s_setprio(0);
+        barrier_lds256();
+        softmax(s, ts, full, pb);
+        if (fetch) dma_tile(t + 2, (it + 2) & (kNB - 1));
+      } else {
+        softmax(s, s_ts, s_full, pb);
+        if (fetch) dma_tile(t + 2, (it + 2) & (kNB - 1));
+        barrier_lds256();
+        __builtin_amdgcn_s_setprio(1);
+        mfma_half(std::true_type{}, vs, ks, pb, s);
+        __builtin_amdgcn_s_setprio(0);
+        s_ts = ts;
+        s_full = full;
+      }
+      if (fetch)
+        wait_loads256_but(n_my_loads);
+      else
+        wait_loads256();
+      barrier_lds256();
+    }
+    // drain: PV of the last tile (group B first runs its softmax)
+    if (GB) softmax(s, s_ts, s_full, pb);
+    barrier_lds256();
+    mfma_half(std::false_type{}, (n_t + kNB - 1) & (kNB - 1), 0, pb, s);
+  };
+  if (wave_u >= kNW / 2)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // Fast pass: a workgroup with a row whose sum leaves [2^-64, 2^64] (extreme
   // gammas, no norm, foreign cache contents) stores nothing and raises its
   // flag; the ONLINE launch redoes it with the running maximum.
   const float lt = xhalf_sum256(l_run);
+  const int le = lane_opaque();
+  const int hge = (le & 31) / P, h2e = le >> 5;
+  const int row_pos_e = wbase + (le & 31) % P;
+  const bool row_ok_e = row_pos_e < chunk_end;
   if (!ONLINE) {
-    const bool bad = row_ok && !(lt >= 0x1p-64f && lt <= 0x1p64f);
+    const bool bad = row_ok_e && !(lt >= 0x1p-64f && lt <= 0x1p64f);
     const int any_bad = __syncthreads_or(bad);
     if (tid == 0) a.flags[li] = any_bad;
     if (any_bad) return;
@@ -359,9 +493,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
 
   // ---- epilogue: O / l to bf16; one swap between the lane halves per word
   // gives each lane dims [32 mb + 16 j + 8 h2, +8), stored as 16 bytes.
-  if (row_ok) {
+  if (row_ok_e) {
     const float inv = 1.f / lt;
-    uint16_t* dst = a.o + (((long long)b * a.S + (row_pos - p0)) * a.Hq + g * G + hg) * kDh + 8 * h2;
+    uint16_t* dst = a.o + (((long long)b * a.S + (row_pos_e - p0)) * a.Hq + g * G + hge) * kDh + 8 * h2e;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
@@ -373,7 +507,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
         // lanes 32..63 receive hi of lane - 32; lanes 0..31 receive lo of lane + 32
         const auto r0 = __builtin_amdgcn_permlane32_swap(lo0, hi0, false, false);
         const auto r1 = __builtin_amdgcn_permlane32_swap(lo1, hi1, false, false);
-        const u32x4 ov = h2 ? u32x4{r0[0], r1[0], hi0, hi1} : u32x4{lo0, lo1, r0[1], r1[1]};
+        const u32x4 ov = h2e ? u32x4{r0[0], r1[0], hi0, hi1} : u32x4{lo0, lo1, r0[1], r1[1]};
         *(u32x4*)(dst + 32 * mb + 16 * j) = ov;
       }
   }
