@@ -91,6 +91,20 @@ __device__ __forceinline__ void dma16_256(const void* src, uint32_t lds_addr) {
       : "v"(src), "s"(lds_addr));
 }
 
+// The same with a wave-uniform base in SGPRs and a 32-bit per-lane byte
+// offset (half the per-lane address operands of the 64-bit form).
+__device__ __forceinline__ void dma16s_256(const void* base, uint32_t off, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_addr));
+}
+
 // A zero K/V row: the source of tile rows whose key does not exist and of
 // pad positions.
 __device__ __attribute__((aligned(256))) uint16_t g_zero_row256[kDh] = {0};
@@ -119,6 +133,7 @@ __device__ __forceinline__ Range256 row_range256(int i, int b, int kmin_avail, c
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 }  // namespace
 
@@ -129,6 +144,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   constexpr int WP = kNW * P;  // positions per workgroup
   __shared__ __attribute__((aligned(1024))) char lds[kNB * kSlotBytes];
   __shared__ __attribute__((aligned(16))) float s_gamma[kDh];
+  // per (wave, load, lane): the (row, chunk * 8) a lane's piece holds, row << 16
+  // | chunk * 8 (pads point at piece 0); the same for every tile
+  __shared__ __attribute__((aligned(16))) uint32_t s_piece[kNW * 5 * 64];
   lds_char* const ldsp = (lds_char*)lds;
   const uint32_t lds0 = (uint32_t)(uintptr_t)ldsp;
 
@@ -179,15 +197,47 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   const int cap = a.cap, is_ring = a.is_ring, has_cache = a.has_cache;
   const uint16_t* ck_bg = has_cache ? a.ck + cache_bg : nullptr;
   const uint16_t* cv_bg = has_cache ? a.cv + cache_bg : nullptr;
-  auto dma_tile = [&](int t, int slot) {
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int k = wave_u + kNW * j;
+    const bool is_v = k >= kKLoads;
+    const int n = 64 * (is_v ? k - kKLoads : k) + lane;
+    const int row = is_v ? n / kVRow : n / kKRow;
+    const int col = is_v ? n - row * kVRow : n - row * kKRow;
+    const bool data = k < kLoads && row < kBNh && col < 32;
+    *(lds_u32*)((lds_char*)s_piece + 4 * ((wave_u * 5 + j) * 64 + lane)) = data ? ((uint32_t)row << 16) | (8 * col) : 0u;
+  }
+  // Load j of this wave (k = wave + 8 j): tiles wholly inside the chunk or
+  // wholly inside a contiguous stretch of the cache take a straight path
+  // (a wave-uniform base plus the lane's piece offset); tiles at the chunk or
+  // cache edges check every row and read a zero row for keys that do not
+  // exist.
+  auto dma_tile = [&](int t, int slot) __attribute__((always_inline)) {
     const int ts = p0 + t * kBNh;
-    const int mode = (t >= 0 && ts + kBNh <= chunk_end) ? 0
-                     : (has_cache && ts >= kmin_avail && ts + kBNh <= p0 && (!is_ring || cap >= kBNh)) ? 1
-                                                                                                      : 2;
-    const int slot0 = (mode == 1 && is_ring) ? ts % cap : ts;
-    // An opaque copy of the lane index: the per-lane piece coordinates are
-    // recomputed at every call instead of being kept in registers across the
-    // tile loop, where O and Q leave no room for them.
+    const bool in_chunk = t >= 0 && ts + kBNh <= chunk_end;
+    const bool in_cache = !in_chunk && has_cache && ts >= kmin_avail && ts + kBNh <= p0;
+    const int slot0 = (in_cache && is_ring) ? ts % cap : ts;
+    const bool cache_run = in_cache && (!is_ring || slot0 + kBNh <= cap);
+    const uint32_t dst0 = lds0 + slot * kSlotBytes;
+    if (in_chunk || cache_run) {
+      const uint16_t* kb = in_chunk ? khat_bg + (long long)t * kBNh * kDh : ck_bg + (long long)slot0 * kDh;
+      const uint16_t* vb = in_chunk ? v_bg + (long long)t * kBNh * vstride : cv_bg + (long long)slot0 * kDh;
+      const int vs = in_chunk ? vstride : kDh;
+      const lds_char* pc = (lds_char*)s_piece + 4 * (wave_u * 5 * 64);
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+#pragma unroll
+      for (int j = 0; j < 5; ++j) {
+        const int k = wave_u + kNW * j;
+        if (k < kLoads) {
+          const uint32_t code = *(const lds_u32*)(pc + 4 * (j * 64 + lane_o));
+          const bool is_v = k >= kKLoads;
+          const uint32_t off = 2u * ((code >> 16) * (uint32_t)(is_v ? vs : kDh) + (code & 0xffffu));
+          dma16s_256(is_v ? vb : kb, off, dst0 + (is_v ? kKBytes + 1024 * (k - kKLoads) : 1024 * k));
+        }
+      }
+      return;
+    }
     int lane_o = lane;
     asm volatile("" : "+v"(lane_o));
 #pragma unroll
@@ -200,34 +250,17 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
         const int row = is_v ? n / kVRow : n / kKRow;
         const int col = is_v ? n - row * kVRow : n - row * kKRow;
         const bool data = row < kBNh && col < 32;
-        // pad positions are never read: in the uniform modes they fetch the
-        // tile's first piece, which exists
-        const int rr = data ? row : 0;
-        const int cc = data ? col : 0;
-        const uint16_t* src;
-        if (mode == 0) {
-          const uint16_t* base = is_v ? v_bg + (long long)t * kBNh * vstride : khat_bg + (long long)t * kBNh * kDh;
-          src = base + (uint32_t)(rr * (is_v ? vstride : kDh) + 8 * cc);
-        } else if (mode == 1 && (!is_ring || slot0 + kBNh <= cap)) {
-          const uint16_t* base = (is_v ? cv_bg : ck_bg) + (long long)slot0 * kDh;
-          src = base + (uint32_t)(rr * kDh + 8 * cc);
-        } else if (mode == 1) {
-          int sl = slot0 + rr;
-          if (sl >= cap) sl -= cap;
-          src = (is_v ? cv_bg : ck_bg) + (long long)sl * kDh + 8 * cc;
-        } else {
-          const int jj = ts + row;
-          src = g_zero_row256;
-          if (data) {
-            if (jj >= p0 && jj < chunk_end) {
-              src = (is_v ? v_bg + (long long)(jj - p0) * vstride : khat_bg + (long long)(jj - p0) * kDh) + 8 * col;
-            } else if (has_cache && jj < p0 && jj >= kmin_avail) {
-              const long long sl = is_ring ? (long long)(jj % cap) : (long long)jj;
-              src = (is_v ? cv_bg : ck_bg) + sl * kDh + 8 * col;
-            }
+        const int jj = ts + row;
+        const uint16_t* src = g_zero_row256;
+        if (data) {
+          if (jj >= p0 && jj < chunk_end) {
+            src = (is_v ? v_bg + (long long)(jj - p0) * vstride : khat_bg + (long long)(jj - p0) * kDh) + 8 * col;
+          } else if (has_cache && jj < p0 && jj >= kmin_avail) {
+            const long long sl = is_ring ? (long long)(jj % cap) : (long long)jj;
+            src = (is_v ? cv_bg : ck_bg) + sl * kDh + 8 * col;
           }
         }
-        dma16_256(src, lds0 + slot * kSlotBytes + (is_v ? kKBytes : 0) + 1024 * kk);
+        dma16_256(src, dst0 + (is_v ? kKBytes : 0) + 1024 * kk);
       }
     }
   };
@@ -242,7 +275,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   // Values derived from the lane index are recomputed where they are used
   // (from an opaque copy of the index) instead of being kept in registers
   // across the tile loop, where O and Q leave no room for them.
-  auto lane_opaque = [&]() {
+  auto lane_opaque = [&]() __attribute__((always_inline)) {
     int l = lane;
     asm volatile("" : "+v"(l));
     return l;
@@ -324,17 +357,17 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   // 2 st + h2 of row ln; V^T (transposing reads): rows 4 (g4 / 2) + w16 / 4
   // (+8 for the second read, +16 for the second 16-key half), piece
   // 4 mb + 2 (g4 & 1) + (w16 & 3) / 2, byte 8 (w16 & 1).
-  auto operand_bases = [&](uint32_t& kbase, uint32_t& vbase) {
+  auto operand_bases = [&](uint32_t& kbase, uint32_t& vbase) __attribute__((always_inline)) {
     const int l = lane_opaque();
     kbase = lds0 + (l & 31) * (16 * kKRow) + 16 * (l >> 5);
     const int g4 = l >> 4, w16 = l & 15;
     vbase = lds0 + kKBytes + (4 * (g4 >> 1) + (w16 >> 2)) * (16 * kVRow) + 16 * (2 * (g4 & 1) + ((w16 & 3) >> 1)) +
             8 * (w16 & 1);
   };
-  auto rd_k = [&](uint32_t kb, int st) -> bf16x8 {
+  auto rd_k = [&](uint32_t kb, int st) __attribute__((always_inline)) -> bf16x8 {
     return *(lds_bf16x8*)((lds_char*)(uintptr_t)kb + 32 * st);
   };
-  auto rd_v = [&](uint32_t vb, int k) -> bf16x8 {
+  auto rd_v = [&](uint32_t vb, int k) __attribute__((always_inline)) -> bf16x8 {
     const int t2 = k >> 3, mb = k & 7;
     lds_char* p = (lds_char*)(uintptr_t)vb + 16 * 16 * kVRow * t2 + 64 * mb;
     const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
@@ -353,7 +386,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
     const uint32_t vb = vbase + vs * kSlotBytes;
     const uint32_t kb = kbase + ks * kSlotBytes;
     bf16x8 op[kAhead + 1];
-    auto rd = [&](int k) { return k < 16 ? rd_v(vb, k) : rd_k(kb, k - 16); };
+    auto rd = [&](int k) __attribute__((always_inline)) { return k < 16 ? rd_v(vb, k) : rd_k(kb, k - 16); };
 #pragma unroll
     for (int k = 0; k < kAhead; ++k) op[k] = rd(k);
     fence256();
@@ -427,7 +460,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   //   group B (waves 4-7): half 1 softmax(it-1),     half 2 PV(it-1) + QK(it)
   // Before the closing barrier of tile it, tile it+1 must have landed.
   // PV(-1) runs with P = 0 on the zeroed V region of slot 3.
-  auto run = [&](auto grp_b_tag) {
+  auto run = [&](auto grp_b_tag) __attribute__((always_inline)) {
     constexpr bool GB = decltype(grp_b_tag)::value;
     f32x16 s;
 #pragma unroll
