@@ -114,6 +114,19 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
       : "=&s"(saved)
       : "v"(src), "s"(lds_addr));
 }
+// The same with a wave-uniform base in SGPRs and a 32-bit per-lane byte
+// offset: fewer per-lane address operands, no 64-bit address arithmetic.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_addr));
+}
 __device__ __forceinline__ uint32_t lds_addr_of(const uint16_t* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)p);
 }
@@ -424,40 +437,44 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   const uint16_t* ck_bg = a.has_cache ? a.ck + cache_bg : nullptr;
   const uint16_t* cv_bg = a.has_cache ? a.cv + cache_bg : nullptr;
   // Instruction k (0..3) of this wave's share of tile t (k < 2: K rows, else
-  // V rows).  Tiles wholly inside the chunk or wholly inside the cache (the
-  // long-context case) take cheap uniform paths; only boundary tiles check
-  // every row.
+  // V rows).  Tiles wholly inside the chunk or inside one contiguous stretch
+  // of the cache (the long-context case) take a straight path: a wave-uniform
+  // base plus a per-lane offset, the mode test hoisted out of the per-load
+  // code.  Only tiles at the chunk or cache edges check every row.
   auto dma_tile = [&](int t, int kbuf, int vbuf) {
     const int ts = p0 + t * kBN;
-    const int mode = (t >= 0 && ts + kBN <= chunk_end) ? 0
-                     : (a.has_cache && ts >= kmin_avail && ts + kBN <= p0 && (!a.is_ring || a.cap >= kBN)) ? 1
-                                                                                                  : 2;
-    // ring slot of the tile's first key (a ring of >= 64 slots wraps at most
-    // once inside a tile)
-    const int slot0 = (mode == 1 && a.is_ring) ? ts % a.cap : ts;
+    const bool in_chunk = t >= 0 && ts + kBN <= chunk_end;
+    const bool in_cache = !in_chunk && a.has_cache && ts >= kmin_avail && ts + kBN <= p0;
+    const int slot0 = (in_cache && a.is_ring) ? ts % a.cap : ts;
+    const bool cache_run = in_cache && (!a.is_ring || slot0 + kBN <= a.cap);
+    if (in_chunk || cache_run) {
+      const uint16_t* kb = in_chunk ? khat_bg + (long long)t * kBN * kD : ck_bg + (long long)slot0 * kD;
+      const uint16_t* vb = in_chunk ? v_bg + (long long)t * kBN * vstride : cv_bg + (long long)slot0 * kD;
+      const int vs = in_chunk ? vstride : kD;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = k & 1;
+        const bool is_v = k >= 2;
+        const int col = ((lane & 15) ^ ((dma_r << 2) | ((2 * wave + i) & 3))) * 8;
+        const int row = 8 * wave + 4 * i + dma_r;
+        const uint16_t* dst = (is_v ? lds_v(vbuf) : lds_k(kbuf)) + (8 * wave_u + 4 * i) * kD;
+        dma16s(is_v ? vb : kb, 2u * (uint32_t)(row * (is_v ? vs : kD) + col), lds_addr_of(dst));
+      }
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int i = k & 1;
       const bool is_v = k >= 2;
       const int col = ((lane & 15) ^ ((dma_r << 2) | ((2 * wave + i) & 3))) * 8;
       const int row = 8 * wave + 4 * i + dma_r;
-      const uint16_t* src;
-      if (mode == 0) {
-        const int r = t * kBN + row;
-        src = is_v ? v_bg + r * vstride : khat_bg + r * kD;
-      } else if (mode == 1) {
-        int slot = slot0 + row;
-        if (a.is_ring && slot >= a.cap) slot -= a.cap;
-        src = (is_v ? cv_bg : ck_bg) + (long long)slot * kD;
-      } else {
-        const int j = ts + row;
-        src = g_zero_row;
-        if (j >= p0 && j < chunk_end) {
-          src = is_v ? v_bg + (j - p0) * vstride : khat_bg + (j - p0) * kD;
-        } else if (a.has_cache && j < p0 && j >= kmin_avail) {
-          const long long slot = a.is_ring ? (long long)(j % a.cap) : (long long)j;
-          src = (is_v ? cv_bg : ck_bg) + slot * kD;
-        }
+      const int j = ts + row;
+      const uint16_t* src = g_zero_row;
+      if (j >= p0 && j < chunk_end) {
+        src = is_v ? v_bg + (j - p0) * vstride : khat_bg + (j - p0) * kD;
+      } else if (a.has_cache && j < p0 && j >= kmin_avail) {
+        const long long slot = a.is_ring ? (long long)(j % a.cap) : (long long)j;
+        src = (is_v ? cv_bg : ck_bg) + slot * kD;
       }
       const uint16_t* dst = (is_v ? lds_v(vbuf) : lds_k(kbuf)) + (8 * wave_u + 4 * i) * kD;
       dma16(src + col, lds_addr_of(dst));
