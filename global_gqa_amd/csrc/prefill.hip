@@ -200,7 +200,9 @@ __device__ __forceinline__ void softmax(f32x16 (&s)[2], WaveState& w, bf16x8 (&p
 #pragma unroll
       for (int r = 0; r < 16; ++r) w.o[mb][r] *= alpha;
   }
-  float rs = 0.f;
+  // row sum as a pairwise tree (dependent depth 5 instead of a 32-add chain,
+  // which next to the other wave's MFMAs was latency-bound)
+  float rs[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     float e[8];
@@ -208,12 +210,12 @@ __device__ __forceinline__ void softmax(f32x16 (&s)[2], WaveState& w, bf16x8 (&p
     for (int i = 0; i < 8; ++i) {
       const float x = s[t >> 1][8 * (t & 1) + i];
       e[i] = fast_exp2(ONLINE ? x - off : x);
-      rs += e[i];
     }
+    rs[t] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     u32x4 u = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
     pb[t] = __builtin_bit_cast(bf16x8, u);
   }
-  w.l += rs;
+  w.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 }
 
 __device__ __forceinline__ bf16x8 read_v(const uint16_t* vl, const TileAddr& ad, int t, int mb) {
