@@ -92,14 +92,21 @@ int decode_slots(const g3_kv_cache* c, int32_t max_position) {
 // 16 units either way).
 // Short caches (a local layer's 1024-slot ring) with at least 512 (sequence,
 // kv head) pairs take one split each: enough workgroups, and no merge pass.
+// With fewer pairs than that a one-unit split can leave most CUs idle (the
+// 1B model's 32 sequences x 1 kv head: 128 workgroups on a 1024-slot ring,
+// each latency-bound), so the split halves, down to 64 slots, until the grid
+// has about 1024 workgroups.
 int decode_split(int n_slots, int32_t B, int32_t Hkv) {
   const int n_units = (n_slots + g3::kDecodeChunk - 1) / g3::kDecodeChunk;
-  if (n_units <= 16 && (long long)B * Hkv >= 512) return n_units * g3::kDecodeChunk;
-  const long long units = (long long)n_units * B * Hkv;
+  const long long pairs = (long long)B * Hkv;
+  if (n_units <= 16 && pairs >= 512) return n_units * g3::kDecodeChunk;
+  const long long units = (long long)n_units * pairs;
   long long k = units / 2048;
   if (k < 1) k = 1;
   if (k > 16) k = 16;
-  return (int)k * g3::kDecodeChunk;
+  int split = (int)k * g3::kDecodeChunk;
+  while (split > 64 && (long long)((n_slots + split - 1) / split) * pairs < 1024) split /= 2;
+  return split;
 }
 int decode_chunks(int n_slots, int32_t B, int32_t Hkv) {
   const int split = decode_split(n_slots, B, Hkv);

@@ -39,15 +39,16 @@ def test_workspace_sizes(L):
     lin = G.KVCacheC(0, 0, 40000, 0)
     # ring: one split (512 sequence x kv-head pairs); linear: positions 0..32768 in splits of 4096 -> 9
     assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(ring)) == 32 * 32 * 1 * 130 * 4
-    # fewer pairs: the ring splits 4 ways (256 slots each)
-    assert L.g3attn_decode_workspace_size(2, 32, 16, 128, 32768, ctypes.byref(ring)) == 2 * 32 * 4 * 130 * 4
+    # fewer pairs (32): the ring splits into 64-slot pieces (16 x 32 = 512 workgroups; 64 slots is the floor)
+    assert L.g3attn_decode_workspace_size(2, 32, 16, 128, 32768, ctypes.byref(ring)) == 2 * 32 * 16 * 130 * 4
     assert L.g3attn_decode_workspace_size(32, 32, 16, 128, 32768, ctypes.byref(lin)) == 32 * 32 * 9 * 130 * 4
     # head dim 256 (Gemma 3 1B: 4 query heads, 1 kv head): keys [1][1][4096][256] bf16, then 8 flags per
     # 256-position tile of G = 1 (8 waves x 32 rows; the most work items any group size gives)
     assert L.g3attn_prefill_workspace_size(1, 4096, 4, 1, 256) == 4096 * 256 * 2 + 16 * 8 * 4
-    # 4 sequence x kv-head pairs over 128 units of 256 slots: too few pairs for longer splits -> 128 splits
+    # 4 sequence x kv-head pairs over 128 units of 256 slots: one-unit splits give 512 workgroups, so the
+    # split halves to 128 slots -> 256 splits (1024 workgroups)
     assert L.g3attn_decode_workspace_size(4, 4, 1, 256, 32767, ctypes.byref(G.KVCacheC(0, 0, 32768, 0))) == \
-        4 * 4 * 128 * 258 * 4
+        4 * 4 * 256 * 258 * 4
     assert L.g3attn_decode_workspace_size(1, 4, 1, 64, 100, ctypes.byref(ring)) == 0
 
 
