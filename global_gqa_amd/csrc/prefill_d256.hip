@@ -438,19 +438,17 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
     }
-    float rs = 0.f;
+    float rs[2];  // row sum as a pairwise tree (short dependent chains)
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       float e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        e[i] = fast_exp2(ONLINE ? s[8 * t2 + i] - off : s[8 * t2 + i]);
-        rs += e[i];
-      }
+      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(ONLINE ? s[8 * t2 + i] - off : s[8 * t2 + i]);
+      rs[t2] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       u32x4 u = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
       pb[t2] = __builtin_bit_cast(bf16x8, u);
     }
-    l_run += rs;
+    l_run += rs[0] + rs[1];
   };
 
   // Ping-pong over the tiles (tile it in slot it % 4; the loads of tile
