@@ -102,30 +102,26 @@ __device__ __forceinline__ void wait_tile_loads_but(int newer) {
 // later LDS read as dependent on it (it cannot tell the tile buffers apart
 // and would wait for all loads in flight); the kernel orders these loads
 // itself with wait_tile_loads_but() before the barrier that publishes a tile.
-// M0 is saved and restored around the load.
+// M0 is declared clobbered (the compiler re-sets it if it ever needs it).
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds_addr));
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds_addr)
+      : "m0");
 }
 // The same with a wave-uniform base in SGPRs and a 32-bit per-lane byte
 // offset: fewer per-lane address operands, no 64-bit address arithmetic.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds_addr));
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds_addr)
+      : "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr_of(const uint16_t* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)p);

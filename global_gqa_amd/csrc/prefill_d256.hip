@@ -77,32 +77,28 @@ __device__ __forceinline__ void wait_loads256_but(int n) {
 __device__ __forceinline__ void fence256() { __builtin_amdgcn_sched_barrier(0); }
 
 // One 16-byte global -> LDS load per lane: lane L writes LDS bytes
-// [lds_addr + 16 L, +16) (global_load_lds_dwordx4, address in M0, which is
-// saved and restored).
+// [lds_addr + 16 L, +16) (global_load_lds_dwordx4, address in M0, declared
+// clobbered).
 __device__ __forceinline__ void dma16_256(const void* src, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds_addr));
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds_addr)
+      : "m0");
 }
 
 // The same with a wave-uniform base in SGPRs and a 32-bit per-lane byte
 // offset (half the per-lane address operands of the 64-bit form).
 __device__ __forceinline__ void dma16s_256(const void* base, uint32_t off, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds_addr));
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds_addr)
+      : "m0");
 }
 
 // A zero K/V row: the source of tile rows whose key does not exist and of
