@@ -12,82 +12,69 @@
 
 namespace g3 {
 
-// 16 lanes per head row; lane j owns dims [E j, E j + E) and
-// [D/2 + E j, D/2 + E j + E) with E = D / 32 (4 for D = 128, 8 for D = 256),
-// so every rotation pair (k, k + D/2) stays inside one lane.
-template <int E>
-struct Vec;
-template <>
-struct Vec<4> {
-  typedef u32x2 T;
-};
-template <>
-struct Vec<8> {
-  typedef u32x4 T;
-};
-
+// D/16 lanes per head row (8 at D = 128, 16 at D = 256); lane j owns dims
+// [8 j, 8 j + 8) and [D/2 + 8 j, D/2 + 8 j + 8), one 16-byte load and store
+// per half, so every rotation pair (k, k + D/2) stays inside one lane.
 template <int D, bool NORM>
 __global__ __launch_bounds__(256) void qknorm_rope_rows(RowsArgs a, Pos0Table p0t, RopeTable rt) {
-  constexpr int E = D / 32;
-  typedef typename Vec<E>::T VT;
-  const int j = threadIdx.x & 15;
-  double rev[E];
+  constexpr int LPR = D / 16;     // lanes per row
+  constexpr int RPB = 256 / LPR;  // rows per workgroup pass
+  const int j = threadIdx.x % LPR;
+  double rev[8];
 #pragma unroll
-  for (int i = 0; i < E; ++i) rev[i] = rt.rev[E * j + i];
-  float gam[2 * E];
+  for (int i = 0; i < 8; ++i) rev[i] = rt.rev[8 * j + i];
+  float gam[16];
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    gam[i] = NORM ? a.gamma[E * j + i] : 1.f;
-    gam[E + i] = NORM ? a.gamma[D / 2 + E * j + i] : 1.f;
+  for (int i = 0; i < 8; ++i) {
+    gam[i] = NORM ? a.gamma[8 * j + i] : 1.f;
+    gam[8 + i] = NORM ? a.gamma[D / 2 + 8 * j + i] : 1.f;
   }
   const long long n_rows = (long long)a.T * a.H;
-  const long long stride = (long long)gridDim.x * 16;
-  for (long long R = (long long)blockIdx.x * 16 + (threadIdx.x >> 4); R < n_rows; R += stride) {
+  const long long stride = (long long)gridDim.x * RPB;
+  for (long long R = (long long)blockIdx.x * RPB + threadIdx.x / LPR; R < n_rows; R += stride) {
     const long long t = R / a.H;
     const int h = (int)(R - t * a.H);
     const int bt = (int)(t / a.S);
     const int st = (int)(t - (long long)bt * a.S);
     const int pos = a.positions ? a.positions[t] : pos0_of(p0t, bt) + st;
     const uint16_t* src = a.in + R * D;
-    const VT lo = *(const VT*)(src + E * j);
-    const VT hi = *(const VT*)(src + D / 2 + E * j);
-    float x[2 * E];
+    const u32x4 lo = *(const u32x4*)(src + 8 * j);
+    const u32x4 hi = *(const u32x4*)(src + D / 2 + 8 * j);
+    float x[16];
 #pragma unroll
-    for (int e = 0; e < E / 2; ++e) {
+    for (int e = 0; e < 4; ++e) {
       x[2 * e] = bf_lo(lo[e]);
       x[2 * e + 1] = bf_hi(lo[e]);
-      x[E + 2 * e] = bf_lo(hi[e]);
-      x[E + 2 * e + 1] = bf_hi(hi[e]);
+      x[8 + 2 * e] = bf_lo(hi[e]);
+      x[8 + 2 * e + 1] = bf_hi(hi[e]);
     }
     if (NORM) {
       float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < 2 * E; ++i) ss += x[i] * x[i];
-      ss += __shfl_xor(ss, 8, 16);
-      ss += __shfl_xor(ss, 4, 16);
-      ss += __shfl_xor(ss, 2, 16);
-      ss += __shfl_xor(ss, 1, 16);
+      for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
+#pragma unroll
+      for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, LPR);
       const float r = __frsqrt_rn(ss * (1.f / D) + a.eps);
 #pragma unroll
-      for (int i = 0; i < 2 * E; ++i) x[i] = x[i] * r * gam[i];
+      for (int i = 0; i < 16; ++i) x[i] = x[i] * r * gam[i];
     }
-    float y[2 * E];
+    float y[16];
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
+    for (int i = 0; i < 8; ++i) {
       float sn, cs;
       rope_sincos(pos, rev[i], sn, cs);
-      y[i] = x[i] * cs - x[E + i] * sn;
-      y[E + i] = x[i] * sn + x[E + i] * cs;
+      y[i] = x[i] * cs - x[8 + i] * sn;
+      y[8 + i] = x[i] * sn + x[8 + i] * cs;
     }
     uint16_t* dst = a.out + (a.head_major ? (((long long)bt * a.H + h) * a.S + st) * D : R * D);
-    VT wlo, whi;
+    u32x4 wlo, whi;
 #pragma unroll
-    for (int e = 0; e < E / 2; ++e) {
+    for (int e = 0; e < 4; ++e) {
       wlo[e] = pack2(y[2 * e], y[2 * e + 1]);
-      whi[e] = pack2(y[E + 2 * e], y[E + 2 * e + 1]);
+      whi[e] = pack2(y[8 + 2 * e], y[8 + 2 * e + 1]);
     }
-    *(VT*)(dst + E * j) = wlo;
-    *(VT*)(dst + D / 2 + E * j) = whi;
+    *(u32x4*)(dst + 8 * j) = wlo;
+    *(u32x4*)(dst + D / 2 + 8 * j) = whi;
   }
 }
 
@@ -123,7 +110,8 @@ static int grid_for(long long work_items, int per_block) {
 
 hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st) {
   // a grid-stride loop over rows: at most 8 workgroups per CU
-  long long grid = ((long long)a.T * a.H + 15) / 16;
+  const int rpb = 256 / (a.D / 16);
+  long long grid = ((long long)a.T * a.H + rpb - 1) / rpb;
   if (grid > 2048) grid = 2048;
   if (a.D == 256) {
     if (a.gamma)
