@@ -54,6 +54,13 @@ def lib() -> ctypes.CDLL:
     L.g3attn_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp, vp, f32, f32,
                                  ctypes.POINTER(Span), i32, ctypes.POINTER(i32), ctypes.POINTER(KVCacheC), vp, sz, vp]
     L.g3attn_prefill.restype = ctypes.c_int
+    L.g3attn_prefill_khat.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp, f32, f32,
+                                      ctypes.POINTER(Span), i32, ctypes.POINTER(i32), ctypes.POINTER(KVCacheC), vp,
+                                      sz, vp]
+    L.g3attn_prefill_khat.restype = ctypes.c_int
+    L.g3attn_qkv_project.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp, f32,
+                                     ctypes.POINTER(i32), vp]
+    L.g3attn_qkv_project.restype = ctypes.c_int
     L.g3attn_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.g3attn_prefill_workspace_size.restype = sz
     L.g3attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, ctypes.POINTER(KVCacheC), i32, i32, f32,
@@ -174,6 +181,18 @@ def _workspace(nbytes, device):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+def _spans_pos0(spans, pos0, B):
+    sp = None
+    n_sp = 0
+    if spans:
+        n_sp = len(spans)
+        sp = (Span * n_sp)(*[Span(int(b), int(s), int(e)) for (b, s, e) in spans])
+    p0 = None
+    if pos0 is not None:
+        p0 = (ctypes.c_int32 * B)(*[int(x) for x in pos0])
+    return sp, n_sp, p0
+
+
 def prefill(q, k, v, layer_kind: int, window: int, rope_base: float, interp_scale: float, q_gamma, k_gamma,
             eps: float, softmax_scale: float = 0.0, spans: Optional[Sequence[Tuple[int, int, int]]] = None,
             pos0: Optional[Sequence[int]] = None, cache: Optional[KVCache] = None, o=None, workspace=None,
@@ -196,20 +215,70 @@ def prefill(q, k, v, layer_kind: int, window: int, rope_base: float, interp_scal
     need = prefill_workspace_size(B, S, Hq, Hkv, D)
     if workspace is None:
         workspace = _workspace(need, q.device)
-    sp = None
-    n_sp = 0
-    if spans:
-        n_sp = len(spans)
-        sp = (Span * n_sp)(*[Span(int(b), int(s), int(e)) for (b, s, e) in spans])
-    p0 = None
-    if pos0 is not None:
-        p0 = (ctypes.c_int32 * B)(*[int(x) for x in pos0])
+    sp, n_sp, p0 = _spans_pos0(spans, pos0, B)
     cc = ctypes.byref(cache.c()) if cache is not None else None
     _check(lib().g3attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, S, Hq, Hkv, D, int(layer_kind), int(window),
                                 float(rope_base), float(interp_scale), _ptr(q_gamma), _ptr(k_gamma), float(eps),
                                 float(softmax_scale), sp, n_sp, p0, cc, workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
     return o
+
+
+def prefill_khat(q, khat, v, layer_kind: int, window: int, rope_base: float, interp_scale: float, q_gamma,
+                 eps: float, softmax_scale: float = 0.0, spans: Optional[Sequence[Tuple[int, int, int]]] = None,
+                 pos0: Optional[Sequence[int]] = None, cache: Optional[KVCache] = None, o=None, workspace=None,
+                 stream=None):
+    """prefill() with the keys already normed and rotated: khat
+    [B, Hkv, S, D] head-major (as qkv_project writes it)."""
+    import torch
+
+    B, S, Hq, D = q.shape
+    Hkv = khat.shape[1]
+    _check_tensor("q", q, torch.bfloat16)
+    _check_tensor("khat", khat, torch.bfloat16, (B, Hkv, S, D))
+    _check_tensor("v", v, torch.bfloat16, (B, S, Hkv, D))
+    _check_tensor("q_gamma", q_gamma, torch.float32, (D,))
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("o", o, torch.bfloat16, q.shape)
+    if workspace is None:
+        workspace = _workspace(prefill_workspace_size(B, S, Hq, Hkv, D), q.device)
+    sp, n_sp, p0 = _spans_pos0(spans, pos0, B)
+    cc = ctypes.byref(cache.c()) if cache is not None else None
+    _check(lib().g3attn_prefill_khat(_ptr(q), _ptr(khat), _ptr(v), _ptr(o), B, S, Hq, Hkv, D, int(layer_kind),
+                                     int(window), float(rope_base), float(interp_scale), _ptr(q_gamma), float(eps),
+                                     float(softmax_scale), sp, n_sp, p0, cc, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
+
+
+def qkv_project(x, w, Hq: int, Hkv: int, rope_base: float, interp_scale: float, k_gamma, eps: float,
+                pos0: Optional[Sequence[int]] = None, q=None, khat=None, v=None, stream=None):
+    """Input projections of one layer with the key prologue fused: x
+    [B, S, d_model] bf16, w [(Hq + 2 Hkv) * 128, d_model] bf16 (Wq, Wk, Wv
+    rows stacked).  Returns (q [B, S, Hq, 128] raw, khat [B, Hkv, S, 128]
+    normed + rotated, v [B, S, Hkv, 128] raw)."""
+    import torch
+
+    B, S, dm = x.shape
+    D = 128
+    _check_tensor("x", x, torch.bfloat16)
+    _check_tensor("w", w, torch.bfloat16, ((Hq + 2 * Hkv) * D, dm))
+    _check_tensor("k_gamma", k_gamma, torch.float32, (D,))
+    if q is None:
+        q = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=x.device)
+    if khat is None:
+        khat = torch.empty((B, Hkv, S, D), dtype=torch.bfloat16, device=x.device)
+    if v is None:
+        v = torch.empty((B, S, Hkv, D), dtype=torch.bfloat16, device=x.device)
+    _check_tensor("q", q, torch.bfloat16, (B, S, Hq, D))
+    _check_tensor("khat", khat, torch.bfloat16, (B, Hkv, S, D))
+    _check_tensor("v", v, torch.bfloat16, (B, S, Hkv, D))
+    _, _, p0 = _spans_pos0(None, pos0, B)
+    _check(lib().g3attn_qkv_project(_ptr(x), _ptr(w), _ptr(q), _ptr(khat), _ptr(v), B, S, dm, Hq, Hkv, D,
+                                    float(rope_base), float(interp_scale), _ptr(k_gamma), float(eps), p0,
+                                    _stream(stream)))
+    return q, khat, v
 
 
 def decode(q, k_new, v_new, positions, max_position: int, cache: KVCache, layer_kind: int, window: int,

@@ -117,6 +117,30 @@ size_t decode_ws(int32_t B, int32_t Hq, int32_t D, int n_chunks) {
   return round_up((size_t)B * Hq * n_chunks * (D + 2) * sizeof(float), 256);
 }
 
+// Per-sequence first positions (NULL: all 0) as the kernels' table.
+int make_pos0(const int32_t* pos0, int32_t B, int32_t S, g3::Pos0Table* out) {
+  g3::Pos0Table& p0t = *out;
+  p0t = g3::Pos0Table{};
+  p0t.uniform = 1;
+  p0t.v[0] = 0;
+  if (pos0) {
+    bool uni = true;
+    for (int b = 0; b < B; ++b) {
+      if (pos0[b] < 0) return fail(G3_EINVAL, "pos0[%d]=%d < 0", b, pos0[b]);
+      if ((long long)pos0[b] + S > (1LL << 30)) return fail(G3_EINVAL, "pos0[%d]+S out of range", b);
+      if (pos0[b] != pos0[0]) uni = false;
+    }
+    if (!uni && B > g3::kMaxBatchPos0)
+      return fail(G3_EUNSUPPORTED, "per-sequence pos0 supports at most %d sequences", g3::kMaxBatchPos0);
+    p0t.uniform = uni ? 1 : 0;
+    if (uni)
+      p0t.v[0] = pos0[0];
+    else
+      for (int b = 0; b < B; ++b) p0t.v[b] = pos0[b];
+  }
+  return G3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,11 +205,18 @@ size_t g3attn_prefill_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t H
   return prefill_ws(B, S, Hkv, D);
 }
 
-int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16* o, int32_t B, int32_t S,
-                   int32_t Hq, int32_t Hkv, int32_t D, int32_t layer_kind, int32_t window, float rope_base,
-                   float interp_scale, const float* q_gamma, const float* k_gamma, float eps, float softmax_scale,
-                   const g3_span* spans, int32_t n_spans, const int32_t* pos0, const g3_kv_cache* cache,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Prefill of one chunk.  With khat_in == NULL the keys k are normed and
+// rotated into the workspace first; otherwise khat_in already holds them
+// (head-major) and the workspace only carries the flash kernel's flags.
+int prefill_impl(const g3_bf16* q, const g3_bf16* k, const g3_bf16* khat_in, const g3_bf16* v, g3_bf16* o,
+                 int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t layer_kind, int32_t window,
+                 float rope_base, float interp_scale, const float* q_gamma, const float* k_gamma, float eps,
+                 float softmax_scale, const g3_span* spans, int32_t n_spans, const int32_t* pos0,
+                 const g3_kv_cache* cache, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   if (int e = check_heads(Hq, Hkv, D)) return e;
   if (B <= 0 || S <= 0) return fail(G3_EINVAL, "B=%d and S=%d must be positive", B, S);
@@ -194,32 +225,17 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
   if (int e = check_rope(rope_base, interp_scale, eps)) return e;
   float sl2;
   if (int e = check_scale(softmax_scale, D, &sl2)) return e;
-  if (!q || !k || !v || !o) return fail(G3_EINVAL, "q, k, v and o must be non-NULL");
-  for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o})
+  const g3_bf16* kk = khat_in ? khat_in : k;
+  if (!q || !kk || !v || !o) return fail(G3_EINVAL, "q, %s, v and o must be non-NULL", khat_in ? "khat" : "k");
+  for (const void* p : {(const void*)q, (const void*)kk, (const void*)v, (const void*)o})
     if (!aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
   if ((long long)B * S * Hq > (1LL << 31) - 1) return fail(G3_EINVAL, "B*S*Hq too large");
   if ((long long)S * Hkv * D > (1LL << 31) - 1)
     return fail(G3_EUNSUPPORTED, "S*Hkv*D=%lld exceeds the 32-bit row offsets of one sequence",
                 (long long)S * Hkv * D);
 
-  g3::Pos0Table p0t{};
-  p0t.uniform = 1;
-  p0t.v[0] = 0;
-  if (pos0) {
-    bool uni = true;
-    for (int b = 0; b < B; ++b) {
-      if (pos0[b] < 0) return fail(G3_EINVAL, "pos0[%d]=%d < 0", b, pos0[b]);
-      if ((long long)pos0[b] + S > (1LL << 30)) return fail(G3_EINVAL, "pos0[%d]+S out of range", b);
-      if (pos0[b] != pos0[0]) uni = false;
-    }
-    if (!uni && B > g3::kMaxBatchPos0)
-      return fail(G3_EUNSUPPORTED, "per-sequence pos0 supports at most %d sequences", g3::kMaxBatchPos0);
-    p0t.uniform = uni ? 1 : 0;
-    if (uni)
-      p0t.v[0] = pos0[0];
-    else
-      for (int b = 0; b < B; ++b) p0t.v[b] = pos0[b];
-  }
+  g3::Pos0Table p0t;
+  if (int e = make_pos0(pos0, B, S, &p0t)) return e;
   auto P0 = [&](int b) { return pos0 ? pos0[b] : 0; };
 
   g3::SpanTable spt{};
@@ -259,12 +275,12 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(G3_EINVAL, "workspace must be 256-byte aligned");
 
   hipStream_t st = (hipStream_t)stream;
-  uint16_t* khat = (uint16_t*)workspace;
+  const uint16_t* khat = khat_in ? khat_in : (const uint16_t*)workspace;
   const g3::RopeTable rt = rope_table(rope_base, interp_scale, D);
-  {
+  if (!khat_in) {
     g3::RowsArgs a{};
     a.in = k;
-    a.out = khat;
+    a.out = (uint16_t*)workspace;
     a.gamma = k_gamma;
     a.positions = nullptr;
     a.eps = eps;
@@ -285,7 +301,7 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
   a.cv = cache ? cache->v : nullptr;
   a.o = o;
   a.q_gamma = q_gamma;
-  a.flags = (int*)((char*)workspace + prefill_ws_keys(B, S, Hkv, D));
+  a.flags = (int*)((char*)workspace + (khat_in ? 0 : prefill_ws_keys(B, S, Hkv, D)));
   a.eps = eps;
   a.B = B;
   a.S = S;
@@ -318,6 +334,73 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
     if (hipError_t e = g3::launch_append_chunk(ap, p0t, st))
       return fail(G3_EHIP, "cache append launch failed: %s", hipGetErrorString(e));
   }
+  return G3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16* o, int32_t B, int32_t S,
+                   int32_t Hq, int32_t Hkv, int32_t D, int32_t layer_kind, int32_t window, float rope_base,
+                   float interp_scale, const float* q_gamma, const float* k_gamma, float eps, float softmax_scale,
+                   const g3_span* spans, int32_t n_spans, const int32_t* pos0, const g3_kv_cache* cache,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k, nullptr, v, o, B, S, Hq, Hkv, D, layer_kind, window, rope_base, interp_scale, q_gamma,
+                      k_gamma, eps, softmax_scale, spans, n_spans, pos0, cache, workspace, workspace_bytes, stream);
+}
+
+int g3attn_prefill_khat(const g3_bf16* q, const g3_bf16* khat, const g3_bf16* v, g3_bf16* o, int32_t B, int32_t S,
+                        int32_t Hq, int32_t Hkv, int32_t D, int32_t layer_kind, int32_t window, float rope_base,
+                        float interp_scale, const float* q_gamma, float eps, float softmax_scale,
+                        const g3_span* spans, int32_t n_spans, const int32_t* pos0, const g3_kv_cache* cache,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!khat) {
+    g_err[0] = 0;
+    return fail(G3_EINVAL, "khat must be non-NULL");
+  }
+  return prefill_impl(q, nullptr, khat, v, o, B, S, Hq, Hkv, D, layer_kind, window, rope_base, interp_scale,
+                      q_gamma, nullptr, eps, softmax_scale, spans, n_spans, pos0, cache, workspace, workspace_bytes,
+                      stream);
+}
+
+int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* khat, g3_bf16* v, int32_t B,
+                       int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, float rope_base,
+                       float interp_scale, const float* k_gamma, float eps, const int32_t* pos0, void* stream) {
+  g_err[0] = 0;
+  if (D != 128) return fail(G3_EUNSUPPORTED, "qkv_project supports head dim 128 only (got D=%d)", D);
+  if (B <= 0 || S <= 0) return fail(G3_EINVAL, "B=%d and S=%d must be positive", B, S);
+  if (Hq <= 0 || Hkv <= 0) return fail(G3_EINVAL, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
+  if (d_model <= 0 || d_model % 64)
+    return fail(G3_EUNSUPPORTED, "d_model=%d must be a positive multiple of 64", d_model);
+  if (int e = check_rope(rope_base, interp_scale, eps)) return e;
+  if (!x || !w || !q || !khat || !v) return fail(G3_EINVAL, "x, w, q, khat and v must be non-NULL");
+  for (const void* p : {(const void*)x, (const void*)w, (const void*)q, (const void*)khat, (const void*)v})
+    if (!aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
+  const long long T = (long long)B * S;
+  if (T * Hq * D > (1LL << 40) || T > (1LL << 31) - 1 - 128) return fail(G3_EINVAL, "B*S too large");
+  if ((long long)Hq + 2LL * Hkv > 65535) return fail(G3_EINVAL, "Hq + 2 Hkv = %lld heads too many", (long long)Hq + 2LL * Hkv);
+  if (128LL * d_model * 2 > (1LL << 32) - 1) return fail(G3_EUNSUPPORTED, "d_model=%d too large", d_model);
+  g3::Pos0Table p0t;
+  if (int e = make_pos0(pos0, B, S, &p0t)) return e;
+  g3::QkvArgs a{};
+  a.x = x;
+  a.w = w;
+  a.q = q;
+  a.khat = khat;
+  a.v = v;
+  a.k_gamma = k_gamma;
+  a.eps = eps;
+  a.T = (int)T;
+  a.S = S;
+  a.K = d_model;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  hipStream_t st = (hipStream_t)stream;
+  if (g_ev_start) hipEventRecord(g_ev_start, st);
+  const hipError_t le = g3::launch_qkv_proj(a, p0t, rope_table(rope_base, interp_scale, D), st);
+  if (le != hipSuccess) return fail(G3_EHIP, "qkv projection launch failed: %s", hipGetErrorString(le));
+  if (g_ev_stop) hipEventRecord(g_ev_stop, st);
   return G3_OK;
 }
 

@@ -69,6 +69,20 @@ struct DecodeArgs {
   float sl2;
 };
 
+// Fused QKV projection (head dimension 128): W is [Hq + 2 Hkv][128][K]
+// (the q, k and v weight matrices stacked, rows = output features), x is
+// [T][K] with T = B S tokens.
+struct QkvArgs {
+  const uint16_t* x;      // [T][K]
+  const uint16_t* w;      // [(Hq + 2 Hkv) * 128][K]
+  uint16_t* q;            // [T][Hq][128] raw
+  uint16_t* khat;         // [B][Hkv][S][128] normed + rotated
+  uint16_t* v;            // [T][Hkv][128] raw
+  const float* k_gamma;   // fp32 [128] or null (no norm)
+  float eps;
+  int T, S, K, Hq, Hkv;
+};
+
 constexpr int kDecodeChunk = 256;  // granularity of split-K decode splits (slots)
 
 hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st);
@@ -78,6 +92,7 @@ hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const Span
 // Head dimension 256 (Gemma 3 1B): 4 waves x 32 query rows per workgroup.
 hipError_t launch_prefill_d256(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt,
                                const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_qkv_proj(const QkvArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
 

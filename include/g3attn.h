@@ -119,6 +119,40 @@ int g3attn_prefill(const g3_bf16* q, const g3_bf16* k, const g3_bf16* v, g3_bf16
 
 size_t g3attn_prefill_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D);
 
+/* The attention layer's input projections with the key prologue fused in:
+ * q = x Wq^T, k = x Wk^T, v = x Wv^T (the layer's q_proj, k_proj and v_proj,
+ * linear maps without bias: "Gemma explained: What's new in Gemma 3", 27B
+ * module print), then k is QK-RMSNormed with k_gamma and rotated by RoPE at
+ * its absolute position (Technical Report, section 2), exactly as the
+ * prologue of g3attn_prefill does, and written head-major for
+ * g3attn_prefill_khat.  Accumulation is fp32; outputs are rounded to bf16
+ * once (k after its norm and rotation).
+ * x: [B][S][d_model] (the normed hidden states entering the layer);
+ * w: [(Hq + 2 Hkv) * D][d_model], the rows of Wq, then Wk, then Wv (each
+ *   row = one output feature, head h's features at rows h*D .. h*D + D-1);
+ * q: [B][S][Hq][D] raw; khat: [B][Hkv][S][D] normed + rotated;
+ * v: [B][S][Hkv][D] raw.  All outputs are written in full.
+ * k_gamma: device fp32 [D] or NULL (no norm); pos0 as in g3attn_prefill.
+ * Supported: D = 128 and d_model a multiple of 64 (else G3_EUNSUPPORTED);
+ *   Hq + 2 Hkv <= 65535 and B*S < 2^31 - 128 (else G3_EINVAL).
+ * The timing hook, when set, brackets the projection kernel. */
+int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* khat, g3_bf16* v,
+                       int32_t B, int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D,
+                       float rope_base, float interp_scale, const float* k_gamma, float eps,
+                       const int32_t* pos0, void* stream);
+
+/* g3attn_prefill with the key prologue already done: khat [B][Hkv][S][D]
+ * holds the chunk's normed and rotated keys (as g3attn_qkv_project writes
+ * them) and is read only.  Every other argument means what it means for
+ * g3attn_prefill (q is still normed and rotated inside the flash kernel);
+ * the workspace is sized by g3attn_prefill_workspace_size as well. */
+int g3attn_prefill_khat(const g3_bf16* q, const g3_bf16* khat, const g3_bf16* v, g3_bf16* o,
+                        int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                        int32_t layer_kind, int32_t window, float rope_base, float interp_scale,
+                        const float* q_gamma, float eps, float softmax_scale,
+                        const g3_span* spans, int32_t n_spans, const int32_t* pos0,
+                        const g3_kv_cache* cache, void* workspace, size_t workspace_bytes, void* stream);
+
 /* One decode step: each sequence b adds one token at position positions[b].
  * q: [B][Hq][D] raw; k_new, v_new: [B][Hkv][D] raw; o: [B][Hq][D].
  * The new key is normed and rotated, written with v_new to its cache slot,
@@ -149,10 +183,11 @@ const char* g3attn_last_error(void);
 int32_t g3attn_version(void);
 
 /* Profiling hook for this thread.  When both are non-NULL (hipEvent_t
- * handles), the next g3attn_prefill / g3attn_decode calls record `start`
- * immediately before and `stop` immediately after the launch of their main
- * kernel (the flash-attention kernel of a prefill, the split-K kernel of a
- * decode), on the call's stream.  Pass NULL, NULL to turn it off. */
+ * handles), the next g3attn_prefill / g3attn_prefill_khat / g3attn_decode /
+ * g3attn_qkv_project calls record `start` immediately before and `stop`
+ * immediately after the launch of their main kernel (the flash-attention
+ * kernel of a prefill, the split-K kernel of a decode, the projection
+ * kernel), on the call's stream.  Pass NULL, NULL to turn it off. */
 int g3attn_set_timing_events(void* start, void* stop);
 
 #ifdef __cplusplus

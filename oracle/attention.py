@@ -178,6 +178,30 @@ def attend(qh, kh, v, mask, softmax_scale: float) -> np.ndarray:
     return out
 
 
+def qkv_project(x, w_q, w_k, w_v, Hq: int, Hkv: int):
+    """Input projections of an attention layer: q = x Wq^T, k = x Wk^T,
+    v = x Wv^T, each output split into heads.
+
+    "Gemma explained: What's new in Gemma 3", 27B module print: q_proj,
+    k_proj and v_proj are Linear maps without bias, 5376 -> 4096 (32 query
+    heads of 128) and 5376 -> 2048 (16 key/value heads of 128).  A Linear map
+    with weight W [out, in] sends x to x W^T.  The print does not show how
+    the output features split into heads; the reading taken is contiguous
+    blocks: feature h * D + d is dimension d of head h.
+
+    x [B, S, d_model]; w_q [Hq * D, d_model]; w_k, w_v [Hkv * D, d_model].
+    Returns (q [B, S, Hq, D], k [B, S, Hkv, D], v [B, S, Hkv, D]) in float64,
+    raw (the QK-norm and RoPE of ``qknorm_rope`` come after).
+    """
+    x = _f64(x)
+    B, S, _ = x.shape
+    D = _f64(w_q).shape[0] // Hq
+    q = (x @ _f64(w_q).T).reshape(B, S, Hq, D)
+    k = (x @ _f64(w_k).T).reshape(B, S, Hkv, D)
+    v = (x @ _f64(w_v).T).reshape(B, S, Hkv, D)
+    return q, k, v
+
+
 def _scale(softmax_scale, D):
     return float(D) ** -0.5 if not softmax_scale else float(softmax_scale)
 

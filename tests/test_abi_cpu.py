@@ -147,3 +147,40 @@ def test_layer_schedule_matches_oracle():
     import oracle
 
     assert [G.layer_kind(i) for i in range(62)] == [oracle.layer_kind(i) for i in range(62)]
+
+
+def test_qkv_project_validation_errors(L):
+    def call(**kw):
+        a = dict(x=FAKE, w=FAKE, q=FAKE, kh=FAKE, v=FAKE, B=1, S=64, dm=256, Hq=4, Hkv=2, D=128, base=1e4,
+                 scale=1.0, eps=1e-6, pos0=None)
+        a.update(kw)
+        return L.g3attn_qkv_project(a["x"], a["w"], a["q"], a["kh"], a["v"], a["B"], a["S"], a["dm"], a["Hq"],
+                                    a["Hkv"], a["D"], a["base"], a["scale"], None, a["eps"], a["pos0"], None)
+    assert call(D=256) == G.G3_EUNSUPPORTED and "128" in _err(L)
+    assert call(dm=100) == G.G3_EUNSUPPORTED and "multiple of 64" in _err(L)
+    assert call(dm=0) == G.G3_EUNSUPPORTED
+    assert call(B=0) == G.G3_EINVAL
+    assert call(S=-1) == G.G3_EINVAL
+    assert call(Hkv=0) == G.G3_EINVAL
+    assert call(base=1.0) == G.G3_EINVAL
+    assert call(eps=-1.0) == G.G3_EINVAL
+    assert call(w=None) == G.G3_EINVAL and "non-NULL" in _err(L)
+    assert call(kh=FAKE + 8) == G.G3_EINVAL and "aligned" in _err(L)
+    assert call(Hq=70000, Hkv=1) == G.G3_EINVAL and "heads" in _err(L)
+    p0 = (ctypes.c_int32 * 1)(-3)
+    assert call(pos0=p0) == G.G3_EINVAL and "pos0" in _err(L)
+
+
+def test_prefill_khat_validation_errors(L):
+    def call(**kw):
+        a = dict(q=FAKE, kh=FAKE, v=FAKE, o=FAKE, B=1, S=64, Hq=4, Hkv=2, D=128, kind=G.LOCAL, window=1024,
+                 ws_bytes=1 << 30, ws=FAKE)
+        a.update(kw)
+        return L.g3attn_prefill_khat(a["q"], a["kh"], a["v"], a["o"], a["B"], a["S"], a["Hq"], a["Hkv"], a["D"],
+                                     a["kind"], a["window"], 1e4, 1.0, None, 1e-6, 0.0, None, 0, None, None, a["ws"],
+                                     a["ws_bytes"], None)
+    assert call(kh=None) == G.G3_EINVAL and "khat" in _err(L)
+    assert call(D=64) == G.G3_EUNSUPPORTED
+    assert call(kind=3) == G.G3_EINVAL
+    assert call(ws_bytes=8) == G.G3_EWORKSPACE
+    assert call(o=FAKE + 4) == G.G3_EINVAL and "aligned" in _err(L)

@@ -15,6 +15,7 @@ _norm_ok = A.rms_norm
 _vis_ok = A.visibility
 _attend_ok = A.attend
 _decode_ok = A.decode
+_qkv_ok = A.qkv_project
 
 
 def rope_wrong_sign(x, positions, base, interp_scale=1.0):
@@ -97,6 +98,26 @@ def decode_ring_off_by_one(q, k_new, v_new, cache_k, cache_v, is_ring, positions
     return _decode_ok(q, k_new, v_new, cache_k, cache_v, is_ring, positions, *a, **kw)
 
 
+def qkv_heads_interleaved(x, w_q, w_k, w_v, Hq, Hkv):
+    q, k, v = _qkv_ok(x, w_q, w_k, w_v, Hq, Hkv)
+    B, S = q.shape[:2]
+    fix = lambda t: t.reshape(B, S, -1).reshape(B, S, t.shape[3], t.shape[2]).swapaxes(2, 3)
+    return fix(q), fix(k), fix(v)
+
+
+def qkv_k_v_swapped(x, w_q, w_k, w_v, Hq, Hkv):
+    return _qkv_ok(x, w_q, w_v, w_k, Hq, Hkv)
+
+
+def qkv_row_of_weight(x, w_q, w_k, w_v, Hq, Hkv):
+    """Reads a square Wq as [in, out] (x Wq instead of x Wq^T)."""
+    q, k, v = _qkv_ok(x, w_q, w_k, w_v, Hq, Hkv)
+    x = np.asarray(x, dtype=np.float64)
+    if w_q.shape[0] == w_q.shape[1]:
+        q = (x @ np.asarray(w_q, dtype=np.float64)).reshape(q.shape)
+    return q, k, v
+
+
 def _all_pins():
     out = []
     for name in dir(P):
@@ -137,6 +158,9 @@ MUTATIONS = [
     ("attend", attend_no_scale),
     ("attend", attend_softmax_wrong_axis),
     ("decode", decode_ring_off_by_one),
+    ("qkv_project", qkv_heads_interleaved),
+    ("qkv_project", qkv_k_v_swapped),
+    ("qkv_project", qkv_row_of_weight),
 ]
 
 

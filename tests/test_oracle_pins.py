@@ -348,3 +348,53 @@ def test_global_position_shift_invariance():
         a = A.prefill(q, k, v, kind, 7, 1e4, 1.0, gq, gk, 1e-6)
         b = A.prefill(q, k, v, kind, 7, 1e4, 1.0, gq, gk, 1e-6, pos0=[100000])
         np.testing.assert_allclose(a, b, rtol=1e-8, atol=1e-9)
+
+
+# ---------------------------------------------------------------- projections
+def test_qkv_project_identity_blocks():
+    """With Wq = I (d_model = Hq D) the queries are the input cut into
+    heads of D consecutive features; Wk = Wv = the first Hkv D rows of I
+    select the leading features."""
+    B, S, Hq, Hkv, D = 2, 3, 4, 2, 8
+    dm = Hq * D
+    x = _rand(B, S, dm)
+    eye = np.eye(dm)
+    q, k, v = A.qkv_project(x, eye, eye[: Hkv * D], 2 * eye[: Hkv * D], Hq, Hkv)
+    for h in range(Hq):
+        np.testing.assert_array_equal(q[:, :, h, :], x[:, :, h * D:(h + 1) * D])
+    for g in range(Hkv):
+        np.testing.assert_array_equal(k[:, :, g, :], x[:, :, g * D:(g + 1) * D])
+        np.testing.assert_array_equal(v[:, :, g, :], 2 * x[:, :, g * D:(g + 1) * D])
+
+
+def test_qkv_project_one_hot_input_reads_a_weight_column():
+    """A token whose input is the unit vector e_i projects to column i of
+    each weight matrix (not row i: the map is x W^T; Wq is square here so
+    that reading it transposed would go unnoticed by the shapes)."""
+    Hq, Hkv, D, dm = 2, 1, 3, 6
+    wq, wk, wv = _rand(Hq * D, dm), _rand(Hkv * D, dm), _rand(Hkv * D, dm)
+    for i in range(dm):
+        x = np.zeros((1, 1, dm))
+        x[0, 0, i] = 1.0
+        q, k, v = A.qkv_project(x, wq, wk, wv, Hq, Hkv)
+        np.testing.assert_array_equal(q.reshape(-1), wq[:, i])
+        np.testing.assert_array_equal(k.reshape(-1), wk[:, i])
+        np.testing.assert_array_equal(v.reshape(-1), wv[:, i])
+
+
+def test_qkv_project_brute_force_tiny():
+    """Scalar loops over (sequence, token, head, dim, input feature)."""
+    rng = np.random.default_rng(7)
+    B, S, Hq, Hkv, D, dm = 2, 3, 2, 1, 3, 5
+    x = rng.standard_normal((B, S, dm))
+    ws = [rng.standard_normal((H * D, dm)) for H in (Hq, Hkv, Hkv)]
+    got = A.qkv_project(x, ws[0], ws[1], ws[2], Hq, Hkv)
+    for out, w, H in zip(got, ws, (Hq, Hkv, Hkv)):
+        for b in range(B):
+            for s in range(S):
+                for h in range(H):
+                    for d in range(D):
+                        acc = 0.0
+                        for i in range(dm):
+                            acc += float(x[b, s, i]) * float(w[h * D + d, i])
+                        assert abs(out[b, s, h, d] - acc) <= 1e-12 * (1 + abs(acc))

@@ -1,0 +1,193 @@
+"""GPU parity of the fused input projection (q/k/v projections with the key
+QK-norm + RoPE in the epilogue) and of the prefill that consumes its keys,
+through the C ABI, against the fp64 oracle on the same seeded inputs.
+
+Gate for the projections: each output element is one bf16 rounding of an
+fp32 result, so |err| <= 2^-8 |ref| (the rounding, 2^-9 relative, with a
+factor 2 of slack) plus a floor of 1e-3 of the row's rms for elements near
+zero (fp32 accumulation over d_model products: about sqrt(d_model) * 2^-24
+of the sum of |x_i w_i|, a few 1e-5 of the rms at d_model = 5376).
+"""
+import numpy as np
+import pytest
+
+import oracle.attention as A
+import workloads as W
+from tests.gpu_util import assert_parity, dev_bf16, dev_f32, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import global_gqa_amd as G  # noqa: E402
+
+D = 128
+
+
+def assert_proj(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+    tol = 2.0 ** -8 * np.abs(ref) + 1e-3 * rms
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} out of tolerance; worst {np.abs(got - ref)[bad].max()}"
+
+
+def _proj_inputs(config, B, S, dm, Hq, Hkv):
+    x = W.host_normal_bf16((B, S, dm), W.seed_of(config, 0, W.T_X))
+    w = W.host_weight_bf16(((Hq + 2 * Hkv) * D, dm), W.seed_of(config, 0, W.T_W))
+    gk = W.host_gamma(D, W.seed_of(config, 0, W.T_GK))
+    gq = W.host_gamma(D, W.seed_of(config, 0, W.T_GQ))
+    return x, w, gq, gk
+
+
+def _split(w, Hq, Hkv):
+    return w[:Hq * D], w[Hq * D:(Hq + Hkv) * D], w[(Hq + Hkv) * D:]
+
+
+def _oracle_khat(k, gk, pos0, base, scale):
+    """[B, S, Hkv, D] raw keys -> [B, Hkv, S, D] normed and rotated."""
+    B, S = k.shape[:2]
+    out = np.empty((B, k.shape[2], S, D))
+    for b in range(B):
+        pos = (0 if pos0 is None else pos0[b]) + np.arange(S)
+        kh = A.qknorm_rope(k[b], gk, W.EPS, pos, base, scale, gk is not None)
+        out[b] = kh.transpose(1, 0, 2)
+    return out
+
+
+@pytest.mark.parametrize("B,S,dm,Hq,Hkv,pos0,base,scale,norm", [
+    (2, 300, 256, 4, 2, [0, 5000], 1e6, 8.0, True),    # ragged token tiles spanning two sequences
+    (1, 1, 64, 2, 1, None, 1e4, 1.0, True),            # one token, one input chunk
+    (3, 77, 128, 8, 1, [9, 9, 9], 1e4, 1.0, False),    # uniform pos0, no norm, two chunks
+    (1, 640, 320, 4, 4, [131000], 1e6, 8.0, True),     # 5 full tiles, odd chunk count, far positions
+])
+def test_qkv_project_matches_oracle(B, S, dm, Hq, Hkv, pos0, base, scale, norm):
+    x, w, _, gk = _proj_inputs(20, B, S, dm, Hq, Hkv)
+    gk = gk if norm else None
+    print(f"qkv_project B={B} S={S} d_model={dm} Hq={Hq} Hkv={Hkv}", flush=True)
+    q, kh, v = G.qkv_project(dev_bf16(x), dev_bf16(w), Hq, Hkv, base, scale,
+                             dev_f32(gk) if norm else None, W.EPS, pos0)
+    torch.cuda.synchronize()
+    wq, wk, wv = _split(w, Hq, Hkv)
+    rq, rk, rv = A.qkv_project(x, wq, wk, wv, Hq, Hkv)
+    assert_proj(host(q), rq, "q")
+    assert_proj(host(v), rv, "v")
+    assert_proj(host(kh), _oracle_khat(rk, gk, pos0, base, scale), "khat")
+
+
+def test_qkv_project_deterministic_and_writes_every_element():
+    B, S, dm, Hq, Hkv = 2, 200, 192, 4, 2
+    x, w, _, gk = _proj_inputs(21, B, S, dm, Hq, Hkv)
+    xd, wd, gkd = dev_bf16(x), dev_bf16(w), dev_f32(gk)
+    outs = []
+    for fill in (float("nan"), 7.0):
+        q = torch.full((B, S, Hq, D), fill, dtype=torch.bfloat16, device="cuda")
+        kh = torch.full((B, Hkv, S, D), fill, dtype=torch.bfloat16, device="cuda")
+        v = torch.full((B, S, Hkv, D), fill, dtype=torch.bfloat16, device="cuda")
+        G.qkv_project(xd, wd, Hq, Hkv, 1e4, 1.0, gkd, W.EPS, None, q=q, khat=kh, v=v)
+        torch.cuda.synchronize()
+        outs.append((q, kh, v))
+    for a, b in zip(*outs):
+        assert bool(torch.isfinite(a.float()).all()), "an output element was left unwritten"
+        assert bool(torch.equal(a, b)), "results differ between identical calls"
+
+
+@pytest.mark.parametrize("kind", [A.LOCAL, A.GLOBAL])
+def test_qkv_project_then_prefill_khat_end_to_end(kind):
+    """x -> projections (keys normed + rotated in the epilogue) -> flash
+    prefill reading those keys, against oracle projections then the oracle
+    prefill; image spans, per-sequence first positions, ragged S."""
+    B, S, dm, Hq, Hkv = 2, 700, 256, 4, 2
+    x, w, gq, gk = _proj_inputs(22, B, S, dm, Hq, Hkv)
+    pos0 = [0, 300]
+    spans = [W.image_spans(S, 2, 91, base=0), W.image_spans(S, 1, 92, base=300)]
+    flat = [(b, s, e) for b in range(B) for (s, e) in spans[b]]
+    base, scale = (W.ROPE_BASE_LOCAL, 1.0) if kind == A.LOCAL else (W.ROPE_BASE_GLOBAL, 8.0)
+    window = 256
+    q, kh, v = G.qkv_project(dev_bf16(x), dev_bf16(w), Hq, Hkv, base, scale, dev_f32(gk), W.EPS, pos0)
+    o = G.prefill_khat(q, kh, v, kind, window, base, scale, dev_f32(gq), W.EPS, 0.0, flat, pos0)
+    torch.cuda.synchronize()
+    wq, wk, wv = _split(w, Hq, Hkv)
+    rq, rk, rv = A.qkv_project(x, wq, wk, wv, Hq, Hkv)
+    ref = A.prefill(rq, rk, rv, kind, window, base, scale, gq, gk, W.EPS, spans=spans, pos0=pos0)
+    assert_parity(host(o), ref, f"qkv -> prefill_khat kind={kind}")
+
+
+def test_prefill_khat_equals_prefill_on_same_keys():
+    """Given the keys that the library's own prologue makes (qknorm_rope in
+    head-major order), prefill_khat and prefill launch the same flash kernel
+    and must agree bit for bit."""
+    B, S, Hq, Hkv = 2, 500, 8, 2
+    rng_q = W.host_normal_bf16((B, S, Hq, D), 31)
+    rng_k = W.host_normal_bf16((B, S, Hkv, D), 32)
+    rng_v = W.host_normal_bf16((B, S, Hkv, D), 33)
+    gq, gk = W.host_gamma(D, 34), W.host_gamma(D, 35)
+    qd, kd, vd = dev_bf16(rng_q), dev_bf16(rng_k), dev_bf16(rng_v)
+    pos0 = [3, 1000]
+    for kind, base, scale in ((A.LOCAL, 1e4, 1.0), (A.GLOBAL, 1e6, 8.0)):
+        o1 = G.prefill(qd, kd, vd, kind, 300, base, scale, dev_f32(gq), dev_f32(gk), W.EPS, pos0=pos0)
+        pos = torch.tensor([p + s for p in pos0 for s in range(S)], dtype=torch.int32, device="cuda")
+        _, kr = G.qknorm_rope(None, kd.view(B * S, Hkv, D), pos, None, dev_f32(gk), W.EPS, base, scale)
+        kh = kr.view(B, S, Hkv, D).permute(0, 2, 1, 3).contiguous()
+        o2 = G.prefill_khat(qd, kh, vd, kind, 300, base, scale, dev_f32(gq), W.EPS, pos0=pos0)
+        torch.cuda.synchronize()
+        assert bool(torch.equal(o1, o2)), f"kind={kind}: prefill_khat differs from prefill"
+
+
+@pytest.mark.parametrize("is_ring,cap", [(True, 1024), (False, 2048)])
+def test_qkv_project_chunks_into_cache(is_ring, cap):
+    """Two 600-token chunks of one local layer: each chunk's keys come from
+    the projection, prefill_khat attends to the cache and appends; the
+    second chunk's output equals rows [600, 1200) of the oracle prefill of
+    the whole 1200 tokens, and the cache holds the oracle's keys."""
+    B, C, dm, Hq, Hkv, window = 1, 600, 128, 4, 2, 1024
+    x, w, gq, gk = _proj_inputs(23, B, 2 * C, dm, Hq, Hkv)
+    base, scale = W.ROPE_BASE_LOCAL, 1.0
+    cache = G.KVCache.empty(B, Hkv, cap, D, is_ring=is_ring)
+    xd, wd = dev_bf16(x), dev_bf16(w)
+    outs = []
+    for c in range(2):
+        xc = xd[:, c * C:(c + 1) * C].contiguous()
+        q, kh, v = G.qkv_project(xc, wd, Hq, Hkv, base, scale, dev_f32(gk), W.EPS, [c * C])
+        outs.append(G.prefill_khat(q, kh, v, A.LOCAL, window, base, scale, dev_f32(gq), W.EPS, pos0=[c * C],
+                                   cache=cache))
+    torch.cuda.synchronize()
+    wq, wk, wv = _split(w, Hq, Hkv)
+    rq, rk, rv = A.qkv_project(x, wq, wk, wv, Hq, Hkv)
+    ref = A.prefill(rq, rk, rv, A.LOCAL, window, base, scale, gq, gk, W.EPS)
+    assert_parity(host(outs[1]), ref[:, C:], f"second chunk ring={is_ring}")
+    assert_parity(host(outs[0]), ref[:, :C], f"first chunk ring={is_ring}")
+    kref = _oracle_khat(rk, gk, None, base, scale)  # [B, Hkv, 2C, D]
+    n = 2 * C
+    pos = np.arange(max(0, n - cap), n)
+    slots = pos % cap if is_ring else pos
+    assert_proj(host(cache.k)[:, :, slots], kref[:, :, pos], "cached keys")
+    assert_proj(host(cache.v)[:, :, slots], rv[:, pos].transpose(0, 2, 1, 3), "cached values")
+
+
+def test_qkv_project_27b_sampled_rows():
+    """The 27B layer shape at the prefill bench size: x [1, 8192, 5376],
+    W [(32 + 2 * 16) * 128, 5376]; the oracle projects 48 sampled tokens
+    (first and last of the sequence and of tiles included) for every head."""
+    B, S, dm, Hq, Hkv = 1, 8192, W.D_MODEL_27B, 32, 16
+    x, w, _, gk = _proj_inputs(24, B, S, dm, Hq, Hkv)
+    base, scale = W.ROPE_BASE_GLOBAL, 8.0
+    print("qkv_project 27B 8192 x 5376", flush=True)
+    q, kh, v = G.qkv_project(dev_bf16(x), dev_bf16(w), Hq, Hkv, base, scale, dev_f32(gk), W.EPS)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([[0, 127, 128, 4095, 8191], rng.integers(0, S, 43)]))
+    wq, wk, wv = _split(w, Hq, Hkv)
+    rq, rk, rv = A.qkv_project(x[:, toks], wq, wk, wv, Hq, Hkv)
+    ti = torch.as_tensor(toks, device="cuda")
+    assert_proj(host(q[:, ti]), rq, "q")
+    assert_proj(host(v[:, ti]), rv, "v")
+    kh_s = host(kh[:, :, ti])  # [B, Hkv, n, D]
+    ref = np.empty_like(kh_s)
+    kn = A.qknorm_rope(rk[0], gk, W.EPS, toks, base, scale, True)  # positions = token indices
+    ref[0] = kn.transpose(1, 0, 2)
+    assert_proj(kh_s, ref, "khat")

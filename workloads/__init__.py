@@ -7,9 +7,13 @@ oracle nor the HIP binding.
 
 Recipe (used everywhere):
   * seed = 1000 * config + 10 * layer + tensor_id, with tensor ids
-    q 0, k 1, v 2, q-gamma 3, k-gamma 4, cache-K 5, cache-V 6, spans 7;
+    q 0, k 1, v 2, q-gamma 3, k-gamma 4, cache-K 5, cache-V 6, spans 7,
+    layer input x 8, stacked projection weight W 9;
   * tensors are standard-normal float32 rounded to bfloat16 by
     round-to-nearest-even; gamma = 1 + 0.1 * N(0, 1) kept in float32;
+    projection weights are N(0, 1) / sqrt(d_model) (fan-in scaling, so that
+    the projected q, k, v have unit scale like the other inputs) rounded to
+    bfloat16;
   * small tensors come from NumPy's PCG64 on the host; the multi-GB KV caches
     of the decode and long-context workloads come from torch's device
     generator (Philox) so that the bench does not spend minutes on the CPU.
@@ -30,7 +34,8 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-T_Q, T_K, T_V, T_GQ, T_GK, T_CK, T_CV, T_SPANS = range(8)
+T_Q, T_K, T_V, T_GQ, T_GK, T_CK, T_CV, T_SPANS, T_X, T_W = range(10)
+D_MODEL_27B = 5376       # hidden size in the 27B print (q_proj 5376 -> 4096)
 
 WINDOW = 1024            # local span (Technical Report, section 1)
 ROPE_BASE_LOCAL = 1.0e4  # Technical Report, section 2 "Long context"
@@ -57,13 +62,21 @@ def host_normal_bf16(shape: Sequence[int], seed: int) -> np.ndarray:
     return bf16_round(g.standard_normal(tuple(shape), dtype=np.float32))
 
 
+def host_weight_bf16(shape: Sequence[int], seed: int) -> np.ndarray:
+    """Projection weight [out, in]: N(0, 1) / sqrt(in) rounded to bf16."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    w = g.standard_normal(tuple(shape), dtype=np.float32) * np.float32(1.0 / np.sqrt(shape[-1]))
+    return bf16_round(w)
+
+
 def host_gamma(D: int, seed: int) -> np.ndarray:
     g = np.random.Generator(np.random.PCG64(seed))
     return (1.0 + 0.1 * g.standard_normal(D, dtype=np.float64)).astype(np.float32)
 
 
-def device_normal_bf16(shape: Sequence[int], seed: int, device="cuda"):
-    """Standard-normal bf16 tensor drawn on the device (torch Philox)."""
+def device_normal_bf16(shape: Sequence[int], seed: int, device="cuda", std: float = 1.0):
+    """Normal bf16 tensor (standard deviation std) drawn on the device
+    (torch Philox)."""
     import torch
 
     gen = torch.Generator(device=device)
@@ -74,7 +87,10 @@ def device_normal_bf16(shape: Sequence[int], seed: int, device="cuda"):
     step = 1 << 26
     for s in range(0, flat.numel(), step):
         n = min(step, flat.numel() - s)
-        flat[s:s + n] = torch.randn(n, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+        r = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+        if std != 1.0:
+            r.mul_(float(std))
+        flat[s:s + n] = r.to(torch.bfloat16)
     return out
 
 
