@@ -12,7 +12,12 @@ One step = one pass of the whole hot path over one batch of synthetic input:
                    interpolation 8) plus the five local layers;
   * prefill_1b and decode_1b : the same two blocks at Gemma 3 1B shapes
                    (Hq=4, Hkv=1, D=256): one 32768-token sequence, and 32
-                   sequences with 32767 cached positions.
+                   sequences with 32767 cached positions;
+  * qkv leg      : the prefill block from the layer input instead: per
+                   layer the fused q/k/v projection of x [8192, 5376] (keys
+                   normed and rotated in its epilogue), then the flash
+                   prefill on those keys; the same projection through
+                   torch's library GEMM is timed beside it for context.
 Beside the steps, once: the whole 62-layer 27B attention stack (52 local,
 10 global) over one 128K sequence, the prompt through chunked prefills of
 4096 tokens and then a decode loop, on per-layer caches (``schedule``).
@@ -47,7 +52,7 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,chunked,prefill_1b,decode_1b")
+    ap.add_argument("--legs", default="prefill,decode,chunked,prefill_1b,decode_1b,qkv")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle-on-host baseline")
     ap.add_argument("--no-schedule", action="store_true", help="skip the 62-layer 128K schedule run")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -164,6 +169,43 @@ def build_chunked_leg(torch, G, W, C):
     return leg
 
 
+def build_qkv_leg(torch, G, W, C):
+    w = W.WORKLOADS[2]
+    c = w.config
+    dm = W.D_MODEL_27B
+    leg = Leg("qkv")
+    leg.unit = "flop"
+    leg.workload = w
+    leg.per_kernel = False
+    leg.gemm = []
+    for l in range(LAYERS):
+        kind = G.layer_kind(l)
+        base = W.ROPE_BASE_GLOBAL if kind == G.GLOBAL else W.ROPE_BASE_LOCAL
+        x = W.device_normal_bf16((w.B, w.S, dm), W.seed_of(c, l, W.T_X))
+        wt = W.device_normal_bf16(((w.Hq + 2 * w.Hkv) * w.D, dm), W.seed_of(c, l, W.T_W), std=dm ** -0.5)
+        gq = torch.from_numpy(W.host_gamma(w.D, W.seed_of(c, l, W.T_GQ))).cuda()
+        gk = torch.from_numpy(W.host_gamma(w.D, W.seed_of(c, l, W.T_GK))).cuda()
+        q = torch.empty((w.B, w.S, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+        kh = torch.empty((w.B, w.Hkv, w.S, w.D), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty((w.B, w.S, w.Hkv, w.D), dtype=torch.bfloat16, device="cuda")
+        o = torch.empty_like(q)
+        ws = torch.empty(G.prefill_workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device="cuda")
+        y = torch.empty((w.B * w.S, wt.shape[0]), dtype=torch.bfloat16, device="cuda")
+
+        def call(x=x, wt=wt, gq=gq, gk=gk, q=q, kh=kh, v=v, o=o, ws=ws, kind=kind, base=base):
+            G.qkv_project(x, wt, w.Hq, w.Hkv, base, 1.0, gk, W.EPS, None, q=q, khat=kh, v=v)
+            if leg.per_kernel:
+                G.set_timing_events(None, None)  # time the projection kernel only
+            G.prefill_khat(q, kh, v, kind, W.WINDOW, base, 1.0, gq, W.EPS, 0.0, None, None, None, o=o, workspace=ws)
+
+        def gemm(x=x, wt=wt, y=y):
+            torch.mm(x.view(w.B * w.S, dm), wt.t(), out=y)  # 2-D GEMM, y = x W^T
+        leg.calls.append(call)
+        leg.gemm.append(gemm)
+        leg.work.append(2.0 * w.B * w.S * dm * (w.Hq + 2 * w.Hkv) * w.D)
+    return leg
+
+
 def run_leg(torch, G, leg, timed, per_kernel=False):
     """Launch the leg's layers.  timed: events bracket the whole leg.
     per_kernel: events bracket each layer's main kernel (recorded by the
@@ -171,6 +213,7 @@ def run_leg(torch, G, leg, timed, per_kernel=False):
     extra event packets between kernels lengthen the leg itself."""
     if timed:
         leg.ev_leg[0].record()
+    leg.per_kernel = per_kernel
     for l, call in enumerate(leg.calls):
         if per_kernel:
             G.set_timing_events(*leg.main_ev[l])
@@ -325,7 +368,7 @@ def main():
     names = [s for s in args.legs.split(",") if s]
     builders = {"prefill": build_prefill_leg, "decode": build_decode_leg, "chunked": build_chunked_leg,
                 "prefill_1b": lambda *a: build_prefill_leg(*a, cfg=9, name="prefill_1b"),
-                "decode_1b": lambda *a: build_decode_leg(*a, cfg=10, name="decode_1b")}
+                "decode_1b": lambda *a: build_decode_leg(*a, cfg=10, name="decode_1b"), "qkv": build_qkv_leg}
     for n in names:
         leg = builders[n](torch, G, W, C)
         leg.ev_leg = _events(torch, 1)[0]
@@ -364,6 +407,20 @@ def main():
             for l in range(LAYERS):
                 main_ms[leg.name][l] += leg.main_ev[l][0].elapsed_time(leg.main_ev[l][1])
     print(f"[bench] {KK} steps of per-kernel timing done", file=sys.stderr, flush=True)
+    gemm_ms = None
+    if any(leg.name == "qkv" for leg in legs):
+        leg = [x for x in legs if x.name == "qkv"][0]
+        for g in leg.gemm:
+            g()
+        ev = _events(torch, 1)[0]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for s in range(KK):
+            for g in leg.gemm:
+                g()
+        ev[1].record()
+        torch.cuda.synchronize()
+        gemm_ms = ev[0].elapsed_time(ev[1]) / (KK * LAYERS)
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -428,6 +485,23 @@ def main():
         if "decode_1b" in by:
             g1["decode"] = decode_summary(by["decode_1b"])
         out["gemma3_1b"] = g1
+    if "qkv" in by:
+        leg = by["qkv"]
+        w = leg.workload
+        ms = leg_ms["qkv"] / K
+        kms = [x / KK for x in main_ms["qkv"]]
+        ach = sum(leg.work) / (sum(kms) * 1e-3) / 1e12
+        out["fused_qkv"] = {
+            "value": ach, "unit": "TFLOP/s", "workload": w.name + " from the layer input",
+            "d_model": W.D_MODEL_27B, "tokens": w.B * w.S, "heads": [w.Hq, w.Hkv, w.Hkv],
+            "block_ms": ms, "projection_flop_per_layer": leg.work[0],
+            "roofline": {"bound": "mfma", "kernel": "qkv_proj", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                         "traffic": _traffic("qkv_proj.hip", "qkv_proj_27b_block"), "launch_ms": kms},
+            "library_gemm": None if gemm_ms is None else {
+                "what": "torch.mm (library GEMM) of the same projection into one [tokens, 8192] output, "
+                        "without the key norm and rotation",
+                "ms": gemm_ms, "TFLOPs": leg.work[0] / (gemm_ms * 1e-3) / 1e12}}
     if out["value"] is None:
         out["value"] = 0.0
     if not args.no_schedule:

@@ -378,9 +378,9 @@ int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* 
   for (const void* p : {(const void*)x, (const void*)w, (const void*)q, (const void*)khat, (const void*)v})
     if (!aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
   const long long T = (long long)B * S;
-  if (T * Hq * D > (1LL << 40) || T > (1LL << 31) - 1 - 128) return fail(G3_EINVAL, "B*S too large");
+  if (T * Hq * D > (1LL << 40) || T > (1LL << 31) - 1 - 256) return fail(G3_EINVAL, "B*S too large");
   if ((long long)Hq + 2LL * Hkv > 65535) return fail(G3_EINVAL, "Hq + 2 Hkv = %lld heads too many", (long long)Hq + 2LL * Hkv);
-  if (128LL * d_model * 2 > (1LL << 32) - 1) return fail(G3_EUNSUPPORTED, "d_model=%d too large", d_model);
+  if (256LL * d_model * 2 > (1LL << 32) - 1) return fail(G3_EUNSUPPORTED, "d_model=%d too large", d_model);
   g3::Pos0Table p0t;
   if (int e = make_pos0(pos0, B, S, &p0t)) return e;
   g3::QkvArgs a{};

@@ -11,19 +11,21 @@
 // every key row) disappears; q and v leave raw (q is normalised inside the
 // prefill kernel).
 //
-// Design (workgroup = 4 waves; tile = one head's 128 output features x 128
-// tokens; grid = (token tiles, Hq + 2 Hkv heads)):
-//   * C^T = W_head X^T with v_mfma_f32_32x32x16_bf16: A = 32 weight rows x 16
+// Design (workgroup = 8 waves; tile = two heads' 256 output features x 256
+// tokens; grid = (token tiles, head pairs)):
+//   * C^T = W X^T with v_mfma_f32_32x32x16_bf16: A = 32 weight rows x 16
 //     inputs, B = 32 token rows x 16 inputs, both contiguous along the input
-//     dimension; wave w owns tokens 32 w .. 32 w + 31 and all 128 features
-//     (4 accumulator blocks), so in the epilogue each lane holds one token's 64
-//     features and the token's other 64 sit in the lane 32 apart: the RMSNorm
-//     is an in-lane sum plus one cross-half swap, and the RoPE pairs
-//     (d, d + 64) are in the same lane;
-//   * 64-input chunks of W and X in LDS, double-buffered (2 x 36 KiB), rows
+//     dimension.  Wave w computes head 2 p + (w & 1) for tokens
+//     64 (w >> 1) .. 64 (w >> 1) + 63: 2 x 4 accumulator blocks, so each
+//     16-input step reads 6 operand fragments from LDS for 8 MFMAs.  In the
+//     epilogue each lane holds one token's 64 features of the head and the
+//     token's other 64 sit in the lane 32 apart: the RMSNorm is an in-lane
+//     sum plus one cross-half swap, and the RoPE pairs (d, d + 64) are in
+//     the same lane;
+//   * 64-input chunks of W and X in LDS, double-buffered (2 x 72 KiB), rows
 //     padded to 144 B (conflict-free ds_read_b128, operand reads at immediate
 //     offsets), filled by global->LDS loads whose per-lane source offsets are
-//     fixed for the whole loop and computed once; two workgroups per CU.
+//     fixed for the whole loop and computed once.
 #include "g3_common.hpp"
 #include "g3_kernels.hpp"
 
@@ -32,13 +34,15 @@ namespace g3 {
 namespace {
 
 constexpr int kQD = 128;                 // head dimension
-constexpr int kQT = 128;                 // tokens per tile
+constexpr int kQT = 256;                 // tokens per tile
+constexpr int kQF = 256;                 // output features per tile (two heads)
 constexpr int kQC = 64;                  // inputs per chunk
 constexpr int kQRow = 9;                 // row stride in 16-byte pieces (128 B data + 16 B pad)
-constexpr int kQLoads = 18;              // 1 KiB loads per 128-row operand tile (128 x 9 pieces)
-constexpr int kQTileB = kQLoads * 1024;  // 18432 bytes
+constexpr int kQLoads = 36;              // 1 KiB loads per 256-row operand tile (256 x 9 pieces)
+constexpr int kQTileB = kQLoads * 1024;  // 36864 bytes
 constexpr int kQStageB = 2 * kQTileB;    // W tile then X tile
-constexpr int kQLoadsPerWave = 9;        // 36 loads per stage over 4 waves
+constexpr int kQWaves = 8;
+constexpr int kQLoadsPerWave = 2 * kQLoads / kQWaves;  // 9
 
 typedef __attribute__((address_space(3))) char qlds_char;
 typedef __attribute__((address_space(3))) const bf16x8 qlds_bf16x8;
@@ -57,90 +61,10 @@ __device__ __forceinline__ void qdma(const void* base, uint32_t off, uint32_t ld
 // __syncthreads would also wait for the next chunk's loads in flight).
 __device__ __forceinline__ void qbarrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-}  // namespace
-
-__global__ __launch_bounds__(256, 2) void qkv_proj(QkvArgs a, Pos0Table p0t, RopeTable rt) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kQStageB];
-  qlds_char* const ldsp = (qlds_char*)lds;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)ldsp;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h2 = lane >> 5, ln = lane & 31;
-  const int t0 = blockIdx.x * kQT;
-  const int head = blockIdx.y;
-  const int K = a.K;
-  const int n_chunks = K / kQC;
-
-  // per-lane source offsets of this wave's 9 loads (load k = wave + 4 j: the
-  // W tile for k < 18, else the X tile); piece n = 64 (k mod 18) + lane is
-  // (row n / 9, 16-byte piece n % 9); the pad piece re-reads piece 0; token
-  // rows past the end re-read the last token (never stored)
-  uint32_t off[kQLoadsPerWave];
-#pragma unroll
-  for (int j = 0; j < kQLoadsPerWave; ++j) {
-    const int k = wave + 4 * j;
-    const bool is_x = k >= kQLoads;
-    const int n = 64 * (is_x ? k - kQLoads : k) + lane;
-    int row = n / kQRow;
-    int pc = n - row * kQRow;
-    if (pc == 8) pc = 0;
-    if (is_x) row = min(row, a.T - 1 - t0);
-    off[j] = 2u * ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)pc);
-  }
-  const uint16_t* wbase = a.w + (long long)head * kQD * K;
-  const uint16_t* xbase = a.x + (long long)t0 * K;
-  auto load_stage = [&](int c, int buf) __attribute__((always_inline)) {
-    const uint32_t dst0 = lds0 + buf * kQStageB;
-#pragma unroll
-    for (int j = 0; j < kQLoadsPerWave; ++j) {
-      const int k = wave + 4 * j;
-      const bool is_x = k >= kQLoads;
-      qdma(is_x ? (const void*)(xbase + c * kQC) : (const void*)(wbase + c * kQC), off[j],
-           dst0 + (is_x ? kQTileB + 1024 * (k - kQLoads) : 1024 * k));
-    }
-  };
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
-
-  // operand bases in a stage: A = weight row 32 b + ln, B = token row
-  // 32 wave + ln, piece 2 st + h2 (+32 b rows and +2 st pieces as immediates)
-  const uint32_t abase = lds0 + ln * (16 * kQRow) + 16 * h2;
-  const uint32_t bbase = lds0 + kQTileB + (32 * wave + ln) * (16 * kQRow) + 16 * h2;
-
-  load_stage(0, 0);
-  if (n_chunks > 1) load_stage(1, 1);
-  for (int c = 0; c < n_chunks; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < n_chunks)
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    qbarrier();  // chunk c is in LDS (this wave's loads waited above)
-    const qlds_char* ap = (qlds_char*)(uintptr_t)(abase + buf * kQStageB);
-    const qlds_char* bp = (qlds_char*)(uintptr_t)(bbase + buf * kQStageB);
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8 bx = *(qlds_bf16x8*)(bp + 32 * st);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const bf16x8 aw = *(qlds_bf16x8*)(ap + 32 * b * 16 * kQRow + 32 * st);
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bx, acc[b], 0, 0, 0);
-      }
-    }
-    qbarrier();  // every wave is done with this buffer
-    if (c + 2 < n_chunks) load_stage(c + 2, buf);
-  }
-
-  // ---- epilogue: lane (ln, h2) holds token t's features
-  // n = 32 b + 8 (r / 4) + 4 h2 + r % 4, b = 0..3, r = 0..15
-  const int t = t0 + 32 * wave + ln;
-  if (t >= a.T) return;
-  const int bt = t / a.S, s = t - bt * a.S;
+// Epilogue of one 32-token block of one head: lane (ln, h2) holds token t's
+// features n = 32 b + 8 (r / 4) + 4 h2 + r % 4 in acc[b][r], b = 0..3.
+__device__ __forceinline__ void store_head_rows(const QkvArgs& a, const Pos0Table& p0t, const RopeTable& rt,
+                                                const f32x16* acc, int head, int t, int h2) {
   if (head < a.Hq || head >= a.Hq + a.Hkv) {
     uint16_t* dst = head < a.Hq ? a.q + ((long long)t * a.Hq + head) * kQD
                                 : a.v + ((long long)t * a.Hkv + (head - a.Hq - a.Hkv)) * kQD;
@@ -156,6 +80,7 @@ __global__ __launch_bounds__(256, 2) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
   }
   // key head: QK-RMSNorm over the 128 features, then RoPE at the token's
   // absolute position, stored head-major [B][Hkv][S][D]
+  const int bt = t / a.S, s = t - bt * a.S;
   float ss = 0.f;
 #pragma unroll
   for (int b = 0; b < 4; ++b)
@@ -192,9 +117,106 @@ __global__ __launch_bounds__(256, 2) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
     }
 }
 
+}  // namespace
+
+__global__ __launch_bounds__(512, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, RopeTable rt) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kQStageB];
+  qlds_char* const ldsp = (qlds_char*)lds;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)ldsp;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, ln = lane & 31;
+  const int wf = wave & 1, wt = wave >> 1;
+  const int t0 = blockIdx.x * kQT;
+  const int f0 = blockIdx.y * kQF;  // first weight row of the tile
+  const int K = a.K;
+  const int n_chunks = K / kQC;
+  const int n_rows = (a.Hq + 2 * a.Hkv) * kQD;
+
+  // per-lane source offsets of this wave's 9 loads (load k = wave + 8 j: the
+  // W tile for k < 36, else the X tile); piece n = 64 (k mod 36) + lane is
+  // (row n / 9, 16-byte piece n % 9); the pad piece re-reads piece 0; rows
+  // past the end (tokens, or the missing second head of an odd head count)
+  // re-read the last row (never stored)
+  uint32_t off[kQLoadsPerWave];
+#pragma unroll
+  for (int j = 0; j < kQLoadsPerWave; ++j) {
+    const int k = wave + kQWaves * j;
+    const bool is_x = k >= kQLoads;
+    const int n = 64 * (is_x ? k - kQLoads : k) + lane;
+    int row = n / kQRow;
+    int pc = n - row * kQRow;
+    if (pc == 8) pc = 0;
+    row = min(row, is_x ? a.T - 1 - t0 : n_rows - 1 - f0);
+    off[j] = 2u * ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)pc);
+  }
+  const uint16_t* wbase = a.w + (long long)f0 * K;
+  const uint16_t* xbase = a.x + (long long)t0 * K;
+  auto load_stage = [&](int c, int buf) __attribute__((always_inline)) {
+    const uint32_t dst0 = lds0 + buf * kQStageB;
+#pragma unroll
+    for (int j = 0; j < kQLoadsPerWave; ++j) {
+      const int k = wave + kQWaves * j;
+      const bool is_x = k >= kQLoads;
+      qdma(is_x ? (const void*)(xbase + c * kQC) : (const void*)(wbase + c * kQC), off[j],
+           dst0 + (is_x ? kQTileB + 1024 * (k - kQLoads) : 1024 * k));
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][b][r] = 0.f;
+
+  // operand bases in a stage: A = weight row 128 wf + 32 b + ln, B = token
+  // row 64 wt + 32 j + ln, piece 2 st + h2 (+32 rows per block and +2 st
+  // pieces as immediates)
+  const uint32_t abase = lds0 + (128 * wf + ln) * (16 * kQRow) + 16 * h2;
+  const uint32_t bbase = lds0 + kQTileB + (64 * wt + ln) * (16 * kQRow) + 16 * h2;
+
+  load_stage(0, 0);
+  if (n_chunks > 1) load_stage(1, 1);
+  for (int c = 0; c < n_chunks; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < n_chunks)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    qbarrier();  // chunk c is in LDS (this wave's loads waited above)
+    const qlds_char* ap = (qlds_char*)(uintptr_t)(abase + buf * kQStageB);
+    const qlds_char* bp = (qlds_char*)(uintptr_t)(bbase + buf * kQStageB);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8 bx[2], aw[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bx[j] = *(qlds_bf16x8*)(bp + 32 * j * 16 * kQRow + 32 * st);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) aw[b] = *(qlds_bf16x8*)(ap + 32 * b * 16 * kQRow + 32 * st);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[j][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[b], bx[j], acc[j][b], 0, 0, 0);
+    }
+    qbarrier();  // every wave is done with this buffer
+    if (c + 2 < n_chunks) load_stage(c + 2, buf);
+  }
+
+  const int head = blockIdx.y * 2 + wf;
+  if (head >= a.Hq + 2 * a.Hkv) return;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = t0 + 64 * wt + 32 * j + ln;
+    if (t < a.T) store_head_rows(a, p0t, rt, acc[j], head, t, h2);
+  }
+}
+
 hipError_t launch_qkv_proj(const QkvArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st) {
-  const dim3 grid((a.T + kQT - 1) / kQT, a.Hq + 2 * a.Hkv);
-  hipLaunchKernelGGL(qkv_proj, grid, dim3(256), 0, st, a, p0t, rt);
+  const dim3 grid((a.T + kQT - 1) / kQT, (a.Hq + 2 * a.Hkv + 1) / 2);
+  hipLaunchKernelGGL(qkv_proj, grid, dim3(64 * kQWaves), 0, st, a, p0t, rt);
   return hipGetLastError();
 }
 

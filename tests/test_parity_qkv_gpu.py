@@ -64,6 +64,8 @@ def _oracle_khat(k, gk, pos0, base, scale):
     (1, 1, 64, 2, 1, None, 1e4, 1.0, True),            # one token, one input chunk
     (3, 77, 128, 8, 1, [9, 9, 9], 1e4, 1.0, False),    # uniform pos0, no norm, two chunks
     (1, 640, 320, 4, 4, [131000], 1e6, 8.0, True),     # 5 full tiles, odd chunk count, far positions
+    (2, 130, 64, 3, 1, [0, 1], 1e4, 1.0, True),        # odd head count: the last head pair has one head
+    (1, 1024, 128, 2, 2, None, 1e6, 8.0, True),        # exact token tiles, no tail
 ])
 def test_qkv_project_matches_oracle(B, S, dm, Hq, Hkv, pos0, base, scale, norm):
     x, w, _, gk = _proj_inputs(20, B, S, dm, Hq, Hkv)
