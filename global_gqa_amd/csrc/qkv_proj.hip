@@ -11,21 +11,32 @@
 // every key row) disappears; q and v leave raw (q is normalised inside the
 // prefill kernel).
 //
-// Design (workgroup = 8 waves; tile = two heads' 256 output features x 256
-// tokens; grid = (token tiles, head pairs)):
+// Design (workgroup = 4 waves, one per SIMD; tile = two heads' 256 output
+// features x 256 tokens; grid = (token tiles, head pairs)):
 //   * C^T = W X^T with v_mfma_f32_32x32x16_bf16: A = 32 weight rows x 16
-//     inputs, B = 32 token rows x 16 inputs, both contiguous along the input
-//     dimension.  Wave w computes head 2 p + (w & 1) for tokens
-//     64 (w >> 1) .. 64 (w >> 1) + 63: 2 x 4 accumulator blocks, so each
-//     16-input step reads 6 operand fragments from LDS for 8 MFMAs.  In the
-//     epilogue each lane holds one token's 64 features of the head and the
-//     token's other 64 sit in the lane 32 apart: the RMSNorm is an in-lane
-//     sum plus one cross-half swap, and the RoPE pairs (d, d + 64) are in
-//     the same lane;
-//   * 64-input chunks of W and X in LDS, double-buffered (2 x 72 KiB), rows
-//     padded to 144 B (conflict-free ds_read_b128, operand reads at immediate
-//     offsets), filled by global->LDS loads whose per-lane source offsets are
-//     fixed for the whole loop and computed once.
+//     inputs, B = 32 token rows x 16 inputs.  Wave w computes head
+//     2 p + (w & 1) for tokens 128 (w >> 1) .. 128 (w >> 1) + 127: 4 x 4
+//     accumulator blocks (256 accumulator registers), 8 operand reads per 16
+//     MFMAs.  In the epilogue each lane holds one token's 64 features of the
+//     head and the token's other 64 sit in the lane 32 apart: the RMSNorm is
+//     an in-lane sum plus one cross-half swap, and the RoPE pairs (d, d + 64)
+//     are in the same lane;
+//   * both operands are consumed in chunks of 32 inputs (two 16-input
+//     steps), staged in LDS by global->LDS loads four chunks deep
+//     (4 x 32 KiB).  Each chunk runs as: the 16 MFMAs of step 0 while the
+//     operands of step 1 are read; the barrier that publishes chunk c + 1;
+//     the 16 MFMAs of step 1 while the operands of step 0 of chunk c + 1 are
+//     read and the loads of chunk c + 4 are issued into the stage chunk c
+//     leaves.  Operand reads and loads sit between MFMAs, so the matrix
+//     pipe keeps running across the barrier;
+//   * rows are 64 B (four 16-byte pieces) with the pieces permuted by
+//     piece ^ sw(row), sw(r) = (r >> 2) & 3: with lane l reading row l % 32,
+//     piece (2 st + l / 32) ^ sw(row), the ds_read_b128 runs in its 4 base
+//     cycles with no bank-conflict cycles (measured with the LDS counters on
+//     gfx950; the unpermuted layout, and other permutations that spread 16
+//     consecutive lanes over the banks, measured 2-4 way conflicts).  sw
+//     depends only on the row's low five bits, so operand blocks 32 rows
+//     apart read at immediate offsets.
 #include "g3_common.hpp"
 #include "g3_kernels.hpp"
 
@@ -33,16 +44,15 @@ namespace g3 {
 
 namespace {
 
-constexpr int kQD = 128;                 // head dimension
-constexpr int kQT = 256;                 // tokens per tile
-constexpr int kQF = 256;                 // output features per tile (two heads)
-constexpr int kQC = 64;                  // inputs per chunk
-constexpr int kQRow = 9;                 // row stride in 16-byte pieces (128 B data + 16 B pad)
-constexpr int kQLoads = 36;              // 1 KiB loads per 256-row operand tile (256 x 9 pieces)
-constexpr int kQTileB = kQLoads * 1024;  // 36864 bytes
-constexpr int kQStageB = 2 * kQTileB;    // W tile then X tile
-constexpr int kQWaves = 8;
-constexpr int kQLoadsPerWave = 2 * kQLoads / kQWaves;  // 9
+constexpr int kQD = 128;                      // head dimension
+constexpr int kQT = 256;                      // tokens per tile
+constexpr int kQF = 256;                      // output features per tile (two heads)
+constexpr int kQC = 32;                       // inputs per chunk
+constexpr int kQStages = 4;                   // chunks staged in LDS
+constexpr int kQTileB = 256 * kQC * 2;        // 16384 bytes: 256 rows x 64 B
+constexpr int kQStageB = 2 * kQTileB;         // W tile then X tile
+constexpr int kQWaves = 4;
+constexpr int kQLoadsPerWave = kQStageB / 1024 / kQWaves;  // 8 global->LDS loads of 1 KiB
 
 typedef __attribute__((address_space(3))) char qlds_char;
 typedef __attribute__((address_space(3))) const bf16x8 qlds_bf16x8;
@@ -58,8 +68,10 @@ __device__ __forceinline__ void qdma(const void* base, uint32_t off, uint32_t ld
 }
 
 // Barrier that waits for this wave's LDS operations only (a full
-// __syncthreads would also wait for the next chunk's loads in flight).
+// __syncthreads would also wait for the loads in flight).
 __device__ __forceinline__ void qbarrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int qswz(int r) { return (r >> 2) & 3; }
 
 // Epilogue of one 32-token block of one head: lane (ln, h2) holds token t's
 // features n = 32 b + 8 (r / 4) + 4 h2 + r % 4 in acc[b][r], b = 0..3.
@@ -119,8 +131,8 @@ __device__ __forceinline__ void store_head_rows(const QkvArgs& a, const Pos0Tabl
 
 }  // namespace
 
-__global__ __launch_bounds__(512, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, RopeTable rt) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kQStageB];
+__global__ __launch_bounds__(256, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, RopeTable rt) {
+  __shared__ __attribute__((aligned(1024))) char lds[kQStages * kQStageB];
   qlds_char* const ldsp = (qlds_char*)lds;
   const uint32_t lds0 = (uint32_t)(uintptr_t)ldsp;
 
@@ -132,84 +144,109 @@ __global__ __launch_bounds__(512, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
   const int f0 = blockIdx.y * kQF;  // first weight row of the tile
   const int K = a.K;
   const int n_chunks = K / kQC;
+  const int last = n_chunks - 1;
   const int n_rows = (a.Hq + 2 * a.Hkv) * kQD;
 
-  // per-lane source offsets of this wave's 9 loads (load k = wave + 8 j: the
-  // W tile for k < 36, else the X tile); piece n = 64 (k mod 36) + lane is
-  // (row n / 9, 16-byte piece n % 9); the pad piece re-reads piece 0; rows
-  // past the end (tokens, or the missing second head of an odd head count)
-  // re-read the last row (never stored)
+  // loads: load k = wave + 4 j (the W tile for k < 16, else the X tile)
+  // fills LDS pieces P = 64 (k mod 16) + lane of its tile: row P / 4, slot
+  // P % 4, which holds input piece (P % 4) ^ sw(row).  Rows past the end
+  // (tokens, or the missing second head of an odd head count) re-read the
+  // last row and are never stored.
   uint32_t off[kQLoadsPerWave];
 #pragma unroll
   for (int j = 0; j < kQLoadsPerWave; ++j) {
     const int k = wave + kQWaves * j;
-    const bool is_x = k >= kQLoads;
-    const int n = 64 * (is_x ? k - kQLoads : k) + lane;
-    int row = n / kQRow;
-    int pc = n - row * kQRow;
-    if (pc == 8) pc = 0;
-    row = min(row, is_x ? a.T - 1 - t0 : n_rows - 1 - f0);
-    off[j] = 2u * ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)pc);
+    const bool is_x = k >= 16;
+    const int P = 64 * (k & 15) + lane;
+    const int r = P >> 2;
+    const int g = (P & 3) ^ qswz(r);
+    const int row = min(r, is_x ? a.T - 1 - t0 : n_rows - 1 - f0);
+    off[j] = 2u * ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)g);
   }
   const uint16_t* wbase = a.w + (long long)f0 * K;
   const uint16_t* xbase = a.x + (long long)t0 * K;
-  auto load_stage = [&](int c, int buf) __attribute__((always_inline)) {
-    const uint32_t dst0 = lds0 + buf * kQStageB;
-#pragma unroll
-    for (int j = 0; j < kQLoadsPerWave; ++j) {
-      const int k = wave + kQWaves * j;
-      const bool is_x = k >= kQLoads;
-      qdma(is_x ? (const void*)(xbase + c * kQC) : (const void*)(wbase + c * kQC), off[j],
-           dst0 + (is_x ? kQTileB + 1024 * (k - kQLoads) : 1024 * k));
-    }
+  auto load_one = [&](int c, int stage, int j) __attribute__((always_inline)) {
+    const int k = wave + kQWaves * j;
+    const bool is_x = k >= 16;
+    qdma(is_x ? (const void*)(xbase + c * kQC) : (const void*)(wbase + c * kQC), off[j],
+         lds0 + stage * kQStageB + (is_x ? kQTileB : 0) + 1024 * (k & 15));
   };
 
-  f32x16 acc[2][4];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][b][r] = 0.f;
 
-  // operand bases in a stage: A = weight row 128 wf + 32 b + ln, B = token
-  // row 64 wt + 32 j + ln, piece 2 st + h2 (+32 rows per block and +2 st
-  // pieces as immediates)
-  const uint32_t abase = lds0 + (128 * wf + ln) * (16 * kQRow) + 16 * h2;
-  const uint32_t bbase = lds0 + kQTileB + (64 * wt + ln) * (16 * kQRow) + 16 * h2;
-
-  load_stage(0, 0);
-  if (n_chunks > 1) load_stage(1, 1);
-  for (int c = 0; c < n_chunks; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < n_chunks)
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    qbarrier();  // chunk c is in LDS (this wave's loads waited above)
-    const qlds_char* ap = (qlds_char*)(uintptr_t)(abase + buf * kQStageB);
-    const qlds_char* bp = (qlds_char*)(uintptr_t)(bbase + buf * kQStageB);
+  // operand addresses of step st (inputs 16 st .. 16 st + 15, lane half h2
+  // = piece 2 st + h2): A = weight row 128 wf + 32 b + ln, B = token row
+  // 128 wt + 32 j + ln; sw depends on ln only, blocks add 2048 bytes
+  uint32_t aaddr[2], baddr[2];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      bf16x8 bx[2], aw[4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bx[j] = *(qlds_bf16x8*)(bp + 32 * j * 16 * kQRow + 32 * st);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) aw[b] = *(qlds_bf16x8*)(ap + 32 * b * 16 * kQRow + 32 * st);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[j][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[b], bx[j], acc[j][b], 0, 0, 0);
-    }
-    qbarrier();  // every wave is done with this buffer
-    if (c + 2 < n_chunks) load_stage(c + 2, buf);
+  for (int st = 0; st < 2; ++st) {
+    const int slot = (2 * st + h2) ^ qswz(ln);
+    aaddr[st] = lds0 + (128 * wf + ln) * 64 + 16 * slot;
+    baddr[st] = lds0 + kQTileB + (128 * wt + ln) * 64 + 16 * slot;
   }
+  auto read_ops = [&](int st, int stage, bf16x8 (&ra)[4], bf16x8 (&rb)[4]) __attribute__((always_inline)) {
+    const qlds_char* ap = (qlds_char*)(uintptr_t)(aaddr[st] + stage * kQStageB);
+    const qlds_char* bp = (qlds_char*)(uintptr_t)(baddr[st] + stage * kQStageB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = *(qlds_bf16x8*)(ap + 2048 * i);
+      rb[i] = *(qlds_bf16x8*)(bp + 2048 * i);
+    }
+  };
+
+  // four chunks in flight before the loop; every chunk issues one more
+  // (past the last chunk the loads re-read the last one into a stage nobody
+  // reads), so the count of loads in flight is the same on every path
+#pragma unroll
+  for (int c = 0; c < kQStages; ++c)
+#pragma unroll
+    for (int j = 0; j < kQLoadsPerWave; ++j) load_one(min(c, last), c, j);
+  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // this wave's loads of chunk 0
+  qbarrier();
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  read_ops(0, 0, a0, b0);
+  int stage = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int nstage = stage == 3 ? 0 : stage + 1;
+    // step 0 of chunk c; read step 1 first so the reads land during the MFMAs
+    read_ops(1, stage, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[j][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[b], b0[j], acc[j][b], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // this wave's loads of chunk c + 1
+    qbarrier();  // chunk c + 1 is in LDS for every wave; every read of chunk c has completed
+    // step 1 of chunk c; read step 0 of chunk c + 1 and refill chunk c's
+    // stage, one load after every other MFMA
+    read_ops(0, nstage, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    const int cl = min(c + kQStages, last);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = i >> 2, b = i & 3;
+      acc[j][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[b], b1[j], acc[j][b], 0, 0, 0);
+      if (i & 1) load_one(cl, stage, i >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage = nstage;
+  }
+  // no global->LDS load may still be landing when the workgroup's LDS is
+  // released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const int head = blockIdx.y * 2 + wf;
   if (head >= a.Hq + 2 * a.Hkv) return;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t = t0 + 64 * wt + 32 * j + ln;
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + 128 * wt + 32 * j + ln;
     if (t < a.T) store_head_rows(a, p0t, rt, acc[j], head, t, h2);
   }
 }
