@@ -11,21 +11,20 @@
 // every key row) disappears; q and v leave raw (q is normalised inside the
 // prefill kernel).
 //
-// Design (workgroup = 4 waves, one per SIMD; tile = two heads' 256 output
+// Design (workgroup = 8 waves, two per SIMD; tile = two heads' 256 output
 // features x 256 tokens; grid = (token tiles, head pairs)):
 //   * C^T = W X^T with v_mfma_f32_32x32x16_bf16: A = 32 weight rows x 16
 //     inputs, B = 32 token rows x 16 inputs.  Wave w computes head
-//     2 p + (w & 1) for tokens 128 (w >> 1) .. 128 (w >> 1) + 127: 4 x 4
-//     accumulator blocks (256 accumulator registers), 8 operand reads per 16
-//     MFMAs.  In the epilogue each lane holds one token's 64 features of the
+//     2 p + (w & 1) for tokens 64 (w >> 1) .. 64 (w >> 1) + 63: 2 x 4
+//     accumulator blocks, 6 operand reads per 8 MFMAs.  In the epilogue each lane holds one token's 64 features of the
 //     head and the token's other 64 sit in the lane 32 apart: the RMSNorm is
 //     an in-lane sum plus one cross-half swap, and the RoPE pairs (d, d + 64)
 //     are in the same lane;
 //   * both operands are consumed in chunks of 32 inputs (two 16-input
 //     steps), staged in LDS by global->LDS loads four chunks deep
-//     (4 x 32 KiB).  Each chunk runs as: the 16 MFMAs of step 0 while the
+//     (4 x 32 KiB).  Each chunk runs as: the 8 MFMAs of step 0 while the
 //     operands of step 1 are read; the barrier that publishes chunk c + 1;
-//     the 16 MFMAs of step 1 while the operands of step 0 of chunk c + 1 are
+//     the 8 MFMAs of step 1 while the operands of step 0 of chunk c + 1 are
 //     read and the loads of chunk c + 4 are issued into the stage chunk c
 //     leaves.  Operand reads and loads sit between MFMAs, so the matrix
 //     pipe keeps running across the barrier;
@@ -51,8 +50,8 @@ constexpr int kQC = 32;                       // inputs per chunk
 constexpr int kQStages = 4;                   // chunks staged in LDS
 constexpr int kQTileB = 256 * kQC * 2;        // 16384 bytes: 256 rows x 64 B
 constexpr int kQStageB = 2 * kQTileB;         // W tile then X tile
-constexpr int kQWaves = 4;
-constexpr int kQLoadsPerWave = kQStageB / 1024 / kQWaves;  // 8 global->LDS loads of 1 KiB
+constexpr int kQWaves = 8;
+constexpr int kQLoadsPerWave = kQStageB / 1024 / kQWaves;  // 4 global->LDS loads of 1 KiB
 
 typedef __attribute__((address_space(3))) char qlds_char;
 typedef __attribute__((address_space(3))) const bf16x8 qlds_bf16x8;
@@ -131,7 +130,7 @@ __device__ __forceinline__ void store_head_rows(const QkvArgs& a, const Pos0Tabl
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, RopeTable rt) {
+__global__ __launch_bounds__(512, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, RopeTable rt) {
   __shared__ __attribute__((aligned(1024))) char lds[kQStages * kQStageB];
   qlds_char* const ldsp = (qlds_char*)lds;
   const uint32_t lds0 = (uint32_t)(uintptr_t)ldsp;
@@ -172,9 +171,9 @@ __global__ __launch_bounds__(256, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
          lds0 + stage * kQStageB + (is_x ? kQTileB : 0) + 1024 * (k & 15));
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -188,16 +187,15 @@ __global__ __launch_bounds__(256, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
   for (int st = 0; st < 2; ++st) {
     const int slot = (2 * st + h2) ^ qswz(ln);
     aaddr[st] = lds0 + (128 * wf + ln) * 64 + 16 * slot;
-    baddr[st] = lds0 + kQTileB + (128 * wt + ln) * 64 + 16 * slot;
+    baddr[st] = lds0 + kQTileB + (64 * wt + ln) * 64 + 16 * slot;
   }
-  auto read_ops = [&](int st, int stage, bf16x8 (&ra)[4], bf16x8 (&rb)[4]) __attribute__((always_inline)) {
+  auto read_ops = [&](int st, int stage, bf16x8 (&ra)[4], bf16x8 (&rb)[2]) __attribute__((always_inline)) {
     const qlds_char* ap = (qlds_char*)(uintptr_t)(aaddr[st] + stage * kQStageB);
     const qlds_char* bp = (qlds_char*)(uintptr_t)(baddr[st] + stage * kQStageB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = *(qlds_bf16x8*)(ap + 2048 * i);
-      rb[i] = *(qlds_bf16x8*)(bp + 2048 * i);
-    }
+    for (int i = 0; i < 4; ++i) ra[i] = *(qlds_bf16x8*)(ap + 2048 * i);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) rb[i] = *(qlds_bf16x8*)(bp + 2048 * i);
   };
 
   // four chunks in flight before the loop; every chunk issues one more
@@ -207,9 +205,9 @@ __global__ __launch_bounds__(256, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
   for (int c = 0; c < kQStages; ++c)
 #pragma unroll
     for (int j = 0; j < kQLoadsPerWave; ++j) load_one(min(c, last), c, j);
-  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // this wave's loads of chunk 0
+  asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // this wave's loads of chunk 0
   qbarrier();
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  bf16x8 a0[4], b0[2], a1[4], b1[2];
   read_ops(0, 0, a0, b0);
   int stage = 0;
   for (int c = 0; c < n_chunks; ++c) {
@@ -218,11 +216,11 @@ __global__ __launch_bounds__(256, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
     read_ops(1, stage, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[j][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[b], b0[j], acc[j][b], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // this wave's loads of chunk c + 1
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // this wave's loads of chunk c + 1
     qbarrier();  // chunk c + 1 is in LDS for every wave; every read of chunk c has completed
     // step 1 of chunk c; read step 0 of chunk c + 1 and refill chunk c's
     // stage, one load after every other MFMA
@@ -230,7 +228,7 @@ __global__ __launch_bounds__(256, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
     __builtin_amdgcn_sched_barrier(0);
     const int cl = min(c + kQStages, last);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int j = i >> 2, b = i & 3;
       acc[j][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[b], b1[j], acc[j][b], 0, 0, 0);
       if (i & 1) load_one(cl, stage, i >> 1);
@@ -245,8 +243,8 @@ __global__ __launch_bounds__(256, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
   const int head = blockIdx.y * 2 + wf;
   if (head >= a.Hq + 2 * a.Hkv) return;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + 128 * wt + 32 * j + ln;
+  for (int j = 0; j < 2; ++j) {
+    const int t = t0 + 64 * wt + 32 * j + ln;
     if (t < a.T) store_head_rows(a, p0t, rt, acc[j], head, t, h2);
   }
 }
