@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
     L.g3attn_qkv_project.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp, f32,
                                      ctypes.POINTER(i32), vp]
     L.g3attn_qkv_project.restype = ctypes.c_int
+    L.g3attn_o_project.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+    L.g3attn_o_project.restype = ctypes.c_int
+    L.g3attn_rmsnorm.argtypes = [vp, vp, vp, f32, vp, i32, i32, vp]
+    L.g3attn_rmsnorm.restype = ctypes.c_int
     L.g3attn_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.g3attn_prefill_workspace_size.restype = sz
     L.g3attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, ctypes.POINTER(KVCacheC), i32, i32, f32,
@@ -279,6 +283,49 @@ def qkv_project(x, w, Hq: int, Hkv: int, rope_base: float, interp_scale: float, 
                                     float(rope_base), float(interp_scale), _ptr(k_gamma), float(eps), p0,
                                     _stream(stream)))
     return q, khat, v
+
+
+def o_project(attn, w_o, y=None, stream=None):
+    """The layer's o_proj: attn [B, S, Hq, D] with Hq * D = in, or [..., in]
+    with fewer than four axes (bf16); w_o [out, in] bf16.  Returns y
+    [B, S, out] or [..., out]."""
+    import torch
+
+    _check_tensor("attn", attn, torch.bfloat16)
+    _check_tensor("w_o", w_o, torch.bfloat16)
+    n_out, n_in = w_o.shape
+    if attn.dim() >= 4 and attn.shape[-2] * attn.shape[-1] == n_in:  # [B, S, Hq, D]
+        lead = attn.shape[:-2]
+    elif attn.shape[-1] == n_in:
+        lead = attn.shape[:-1]
+    else:
+        raise ValueError(f"attn shape {tuple(attn.shape)} does not end in in_features {n_in} or [Hq, D]")
+    T = attn.numel() // n_in
+    if y is None:
+        y = torch.empty(tuple(lead) + (n_out,), dtype=torch.bfloat16, device=attn.device)
+    _check_tensor("y", y, torch.bfloat16)
+    if y.numel() != T * n_out:
+        raise ValueError(f"y has {y.numel()} elements, expected {T * n_out}")
+    _check(lib().g3attn_o_project(_ptr(attn), _ptr(w_o), _ptr(y), T, n_in, n_out, _stream(stream)))
+    return y
+
+
+def rmsnorm(x, gamma, eps: float, residual=None, out=None, stream=None):
+    """out = residual + x / sqrt(mean(x^2) + eps) * gamma over the last axis
+    (residual and gamma optional); out may be x or residual."""
+    import torch
+
+    W = x.shape[-1]
+    T = x.numel() // W
+    _check_tensor("x", x, torch.bfloat16)
+    _check_tensor("residual", residual, torch.bfloat16, x.shape)
+    _check_tensor("gamma", gamma, torch.float32, (W,))
+    if out is None:
+        out = torch.empty_like(x)
+    _check_tensor("out", out, torch.bfloat16, x.shape)
+    _check(lib().g3attn_rmsnorm(_ptr(x), _ptr(residual), _ptr(gamma), float(eps), _ptr(out), T, W,
+                                _stream(stream)))
+    return out
 
 
 def decode(q, k_new, v_new, positions, max_position: int, cache: KVCache, layer_kind: int, window: int,

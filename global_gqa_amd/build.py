@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libg3attn.so")
 
-SOURCES = ["api.cpp", "qknorm_rope.hip", "prefill.hip", "prefill_d256.hip", "decode.hip", "qkv_proj.hip"]
+SOURCES = ["api.cpp", "qknorm_rope.hip", "prefill.hip", "prefill_d256.hip", "decode.hip", "qkv_proj.hip", "rmsnorm.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled on purpose: the kernels are written with
 # ordinary scalar fp32 arithmetic and rely on no v_pk_*_f32 instructions.

@@ -364,6 +364,65 @@ int g3attn_prefill_khat(const g3_bf16* q, const g3_bf16* khat, const g3_bf16* v,
                       stream);
 }
 
+int g3attn_o_project(const g3_bf16* attn, const g3_bf16* w_o, g3_bf16* y, int32_t T, int32_t in_features,
+                     int32_t out_features, void* stream) {
+  g_err[0] = 0;
+  if (T <= 0) return fail(G3_EINVAL, "T=%d must be positive", T);
+  if (in_features <= 0 || in_features % 64)
+    return fail(G3_EUNSUPPORTED, "in_features=%d must be a positive multiple of 64", in_features);
+  if (out_features <= 0 || out_features % 128)
+    return fail(G3_EUNSUPPORTED, "out_features=%d must be a positive multiple of 128", out_features);
+  if (out_features / 128 > 2 * 65535) return fail(G3_EINVAL, "out_features=%d too large", out_features);
+  if (!attn || !w_o || !y) return fail(G3_EINVAL, "attn, w_o and y must be non-NULL");
+  for (const void* p : {(const void*)attn, (const void*)w_o, (const void*)y})
+    if (!aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
+  if ((long long)T > (1LL << 31) - 1 - 256) return fail(G3_EINVAL, "T too large");
+  if (256LL * in_features * 2 > (1LL << 32) - 1) return fail(G3_EUNSUPPORTED, "in_features=%d too large", in_features);
+  // the projection kernel with no key/value heads is a plain GEMM y = attn W_o^T
+  // whose [T][out / 128][128] output is y's [T][out] layout
+  g3::QkvArgs a{};
+  a.x = attn;
+  a.w = w_o;
+  a.q = y;
+  a.T = T;
+  a.S = T;
+  a.K = in_features;
+  a.Hq = out_features / 128;
+  a.Hkv = 0;
+  g3::Pos0Table p0t{};
+  p0t.uniform = 1;
+  g3::RopeTable rt{};
+  hipStream_t st = (hipStream_t)stream;
+  if (g_ev_start) hipEventRecord(g_ev_start, st);
+  const hipError_t le = g3::launch_qkv_proj(a, p0t, rt, st);
+  if (le != hipSuccess) return fail(G3_EHIP, "o projection launch failed: %s", hipGetErrorString(le));
+  if (g_ev_stop) hipEventRecord(g_ev_stop, st);
+  return G3_OK;
+}
+
+int g3attn_rmsnorm(const g3_bf16* x, const g3_bf16* residual, const float* gamma, float eps, g3_bf16* out, int32_t T,
+                   int32_t width, void* stream) {
+  g_err[0] = 0;
+  if (T <= 0) return fail(G3_EINVAL, "T=%d must be positive", T);
+  if (width <= 0 || width % 8 || width > g3::rmsnorm_max_width())
+    return fail(G3_EUNSUPPORTED, "width=%d must be a positive multiple of 8 up to %d", width, g3::rmsnorm_max_width());
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(G3_EINVAL, "eps must be >= 0 (got %g)", eps);
+  if (!x || !out) return fail(G3_EINVAL, "x and out must be non-NULL");
+  for (const void* p : {(const void*)x, (const void*)residual, (const void*)out})
+    if (p && !aligned16(p)) return fail(G3_EINVAL, "tensor pointers must be 16-byte aligned");
+  g3::NormArgs a{};
+  a.x = x;
+  a.residual = residual;
+  a.gamma = gamma;
+  a.out = out;
+  a.eps = eps;
+  a.T = T;
+  a.W = width;
+  if (hipError_t e = g3::launch_rmsnorm(a, (hipStream_t)stream))
+    return fail(G3_EHIP, "rmsnorm launch failed: %s", hipGetErrorString(e));
+  return G3_OK;
+}
+
 int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* khat, g3_bf16* v, int32_t B,
                        int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, float rope_base,
                        float interp_scale, const float* k_gamma, float eps, const int32_t* pos0, void* stream) {

@@ -83,6 +83,16 @@ struct QkvArgs {
   int T, S, K, Hq, Hkv;
 };
 
+// Row RMSNorm over the model width with an optional residual add.
+struct NormArgs {
+  const uint16_t* x;         // [T][W]
+  const uint16_t* residual;  // [T][W] or null
+  const float* gamma;        // fp32 [W] or null (gamma = 1)
+  uint16_t* out;             // [T][W]; may alias x or residual
+  float eps;
+  int T, W;                  // W: multiple of 8, at most rmsnorm_max_width()
+};
+
 constexpr int kDecodeChunk = 256;  // granularity of split-K decode splits (slots)
 
 hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st);
@@ -93,6 +103,8 @@ hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const Span
 hipError_t launch_prefill_d256(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt,
                                const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_qkv_proj(const QkvArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st);
+hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t st);
+int rmsnorm_max_width();
 hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
 

@@ -141,6 +141,29 @@ int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* 
                        float rope_base, float interp_scale, const float* k_gamma, float eps,
                        const int32_t* pos0, void* stream);
 
+/* The layer's output projection o_proj: y = attn W_o^T ("Gemma explained:
+ * What's new in Gemma 3", 27B module print: Linear 4096 -> 5376, no bias),
+ * fp32 accumulation, y rounded to bf16 once.
+ * attn: [T][in_features] (the attention output [B][S][Hq][D] seen as rows of
+ *   Hq * D); w_o: [out_features][in_features]; y: [T][out_features].
+ * Supported: in_features a multiple of 64 and out_features a multiple of 128
+ *   (else G3_EUNSUPPORTED).  The timing hook, when set, brackets the kernel. */
+int g3attn_o_project(const g3_bf16* attn, const g3_bf16* w_o, g3_bf16* y, int32_t T,
+                     int32_t in_features, int32_t out_features, void* stream);
+
+/* Row RMSNorm over the model width with an optional residual add, for the
+ * layer's input_layernorm (before q/k/v projection) and
+ * post_attention_layernorm (after o_proj, then added to the residual
+ * stream): Technical Report, section 2 (pre-norm and post-norm with
+ * RMSNorm); "Gemma explained" 27B print (RMSNorm over 5376, eps 1e-6).
+ *   out[t] = residual[t] + x[t] / sqrt(mean(x[t]^2) + eps) * gamma
+ * x, residual (NULL: no residual), out: [T][width] bf16; out may alias x or
+ * residual.  gamma: device fp32 [width] or NULL (gamma = 1).  Sums in fp32,
+ * out rounded to bf16 once.  Supported: width a multiple of 8 up to 8192
+ * (else G3_EUNSUPPORTED). */
+int g3attn_rmsnorm(const g3_bf16* x, const g3_bf16* residual, const float* gamma, float eps,
+                   g3_bf16* out, int32_t T, int32_t width, void* stream);
+
 /* g3attn_prefill with the key prologue already done: khat [B][Hkv][S][D]
  * holds the chunk's normed and rotated keys (as g3attn_qkv_project writes
  * them) and is read only.  Every other argument means what it means for
@@ -184,10 +207,10 @@ int32_t g3attn_version(void);
 
 /* Profiling hook for this thread.  When both are non-NULL (hipEvent_t
  * handles), the next g3attn_prefill / g3attn_prefill_khat / g3attn_decode /
- * g3attn_qkv_project calls record `start` immediately before and `stop`
- * immediately after the launch of their main kernel (the flash-attention
- * kernel of a prefill, the split-K kernel of a decode, the projection
- * kernel), on the call's stream.  Pass NULL, NULL to turn it off. */
+ * g3attn_qkv_project / g3attn_o_project calls record `start` immediately
+ * before and `stop` immediately after the launch of their main kernel (the
+ * flash-attention kernel of a prefill, the split-K kernel of a decode, the
+ * projection kernel), on the call's stream.  Pass NULL, NULL to turn it off. */
 int g3attn_set_timing_events(void* start, void* stop);
 
 #ifdef __cplusplus

@@ -202,6 +202,51 @@ def qkv_project(x, w_q, w_k, w_v, Hq: int, Hkv: int):
     return q, k, v
 
 
+def o_project(attn, w_o):
+    """The layer's output projection: y = attn W_o^T over the concatenated
+    heads.
+
+    "Gemma explained: What's new in Gemma 3", 27B module print: o_proj is a
+    Linear map 4096 -> 5376 without bias, i.e. the Hq heads of D values are
+    read as one vector of Hq * D (head-major, the same contiguous-block
+    reading as the input projections).  attn [..., Hq, D]; w_o [out, Hq * D].
+    Returns y [..., out] in float64.
+    """
+    a = _f64(attn)
+    a = a.reshape(a.shape[:-2] + (a.shape[-2] * a.shape[-1],))
+    return a @ _f64(w_o).T
+
+
+def residual_rms_norm(x, gamma, eps: float, residual=None):
+    """residual + RMSNorm(x) over the model width.
+
+    Technical Report, section 2: Gemma 3 uses RMSNorm both before (pre-norm)
+    and after (post-norm) the attention; the 27B print lists
+    input_layernorm and post_attention_layernorm, RMSNorm over 5376 with
+    eps 1e-6.  The reading taken for the residual stream: the layer maps x to
+    x + post_attention_layernorm(o_proj(attention(input_layernorm(x)))), so
+    the post-norm output is added to the residual and the pre-norm has none.
+    """
+    y = rms_norm(x, gamma, eps)
+    return y if residual is None else _f64(residual) + y
+
+
+def attention_block(x, w_q, w_k, w_v, w_o, Hq: int, Hkv: int, gamma_in, gamma_post, q_gamma, k_gamma,
+                    eps: float, kind: int, window: int, rope_base: float, interp_scale: float,
+                    softmax_scale=None, spans=None, pos0=None):
+    """One attention sublayer from its input: x + post_norm(o_proj(attn(pre_norm(x)))).
+
+    x [B, S, d_model]; the steps are ``residual_rms_norm`` (no residual),
+    ``qkv_project``, ``prefill`` and ``o_project``, then
+    ``residual_rms_norm`` with x as the residual.  Returns [B, S, d_model].
+    """
+    h = residual_rms_norm(x, gamma_in, eps)
+    q, k, v = qkv_project(h, w_q, w_k, w_v, Hq, Hkv)
+    a = prefill(q, k, v, kind, window, rope_base, interp_scale, q_gamma, k_gamma, eps, softmax_scale, spans, pos0)
+    y = o_project(a, w_o)
+    return residual_rms_norm(y, gamma_post, eps, residual=x)
+
+
 def _scale(softmax_scale, D):
     return float(D) ** -0.5 if not softmax_scale else float(softmax_scale)
 

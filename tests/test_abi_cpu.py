@@ -184,3 +184,26 @@ def test_prefill_khat_validation_errors(L):
     assert call(kind=3) == G.G3_EINVAL
     assert call(ws_bytes=8) == G.G3_EWORKSPACE
     assert call(o=FAKE + 4) == G.G3_EINVAL and "aligned" in _err(L)
+
+
+def test_o_project_and_rmsnorm_validation_errors(L):
+    def oproj(**kw):
+        a = dict(attn=FAKE, w=FAKE, y=FAKE, T=64, n_in=4096, n_out=5376)
+        a.update(kw)
+        return L.g3attn_o_project(a["attn"], a["w"], a["y"], a["T"], a["n_in"], a["n_out"], None)
+    assert oproj(n_in=100) == G.G3_EUNSUPPORTED and "multiple of 64" in _err(L)
+    assert oproj(n_out=200) == G.G3_EUNSUPPORTED and "multiple of 128" in _err(L)
+    assert oproj(T=0) == G.G3_EINVAL
+    assert oproj(w=None) == G.G3_EINVAL
+    assert oproj(y=FAKE + 2) == G.G3_EINVAL and "aligned" in _err(L)
+
+    def norm(**kw):
+        a = dict(x=FAKE, res=None, out=FAKE, T=4, W=5376, eps=1e-6)
+        a.update(kw)
+        return L.g3attn_rmsnorm(a["x"], a["res"], None, a["eps"], a["out"], a["T"], a["W"], None)
+    assert norm(W=5377) == G.G3_EUNSUPPORTED
+    assert norm(W=16384) == G.G3_EUNSUPPORTED and "8192" in _err(L)
+    assert norm(T=0) == G.G3_EINVAL
+    assert norm(eps=-1.0) == G.G3_EINVAL
+    assert norm(out=None) == G.G3_EINVAL
+    assert norm(res=FAKE + 4) == G.G3_EINVAL and "aligned" in _err(L)

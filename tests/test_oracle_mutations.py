@@ -16,6 +16,8 @@ _vis_ok = A.visibility
 _attend_ok = A.attend
 _decode_ok = A.decode
 _qkv_ok = A.qkv_project
+_oproj_ok = A.o_project
+_rres_ok = A.residual_rms_norm
 
 
 def rope_wrong_sign(x, positions, base, interp_scale=1.0):
@@ -118,6 +120,15 @@ def qkv_row_of_weight(x, w_q, w_k, w_v, Hq, Hkv):
     return q, k, v
 
 
+def o_project_heads_interleaved(attn, w_o):
+    a = np.asarray(attn, dtype=np.float64)
+    return _oproj_ok(np.swapaxes(a, -1, -2).copy().reshape(a.shape), w_o)
+
+
+def residual_dropped(x, gamma, eps, residual=None):
+    return _rres_ok(x, gamma, eps)
+
+
 def _all_pins():
     out = []
     for name in dir(P):
@@ -161,6 +172,8 @@ MUTATIONS = [
     ("qkv_project", qkv_heads_interleaved),
     ("qkv_project", qkv_k_v_swapped),
     ("qkv_project", qkv_row_of_weight),
+    ("o_project", o_project_heads_interleaved),
+    ("residual_rms_norm", residual_dropped),
 ]
 
 

@@ -398,3 +398,64 @@ def test_qkv_project_brute_force_tiny():
                         for i in range(dm):
                             acc += float(x[b, s, i]) * float(w[h * D + d, i])
                         assert abs(out[b, s, h, d] - acc) <= 1e-12 * (1 + abs(acc))
+
+
+def test_o_project_identity_one_hot_and_brute_force():
+    """o_proj reads the heads as one head-major vector: with W_o = I the output
+    is the heads concatenated; a one-hot attention output picks a column of
+    W_o; scalar loops agree."""
+    rng = np.random.default_rng(8)
+    B, S, Hq, D = 2, 3, 2, 4
+    a = rng.standard_normal((B, S, Hq, D))
+    np.testing.assert_array_equal(A.o_project(a, np.eye(Hq * D)), a.reshape(B, S, Hq * D))
+    w = rng.standard_normal((Hq * D, Hq * D))  # square, so a transposed read would not fail on shape
+    for h in range(Hq):
+        for d in range(D):
+            e = np.zeros((1, 1, Hq, D))
+            e[0, 0, h, d] = 1.0
+            np.testing.assert_array_equal(A.o_project(e, w).reshape(-1), w[:, h * D + d])
+    w = rng.standard_normal((5, Hq * D))
+    y = A.o_project(a, w)
+    for b in range(B):
+        for s in range(S):
+            for o in range(5):
+                acc = 0.0
+                for h in range(Hq):
+                    for d in range(D):
+                        acc += float(a[b, s, h, d]) * float(w[o, h * D + d])
+                assert abs(y[b, s, o] - acc) <= 1e-12 * (1 + abs(acc))
+
+
+def test_residual_rms_norm_closed_forms():
+    """Without a residual it is the RMSNorm; with one it adds it; RMSNorm of a
+    zero row is zero, so a zero sublayer output leaves the residual stream
+    unchanged (the block is then the identity)."""
+    x = _rand(3, 16)
+    g = 1 + 0.1 * _rand(16)
+    r = _rand(3, 16)
+    np.testing.assert_array_equal(A.residual_rms_norm(x, g, 1e-6), A.rms_norm(x, g, 1e-6))
+    np.testing.assert_allclose(A.residual_rms_norm(x, g, 1e-6, residual=r) - r, A.rms_norm(x, g, 1e-6),
+                               rtol=0, atol=1e-12)
+    c = np.full((1, 16), -3.0)  # constant row: mean square 9, so every value maps to -1 * gamma
+    np.testing.assert_allclose(A.residual_rms_norm(c, g, 0.0, residual=r[:1]), r[:1] - g[None, :], atol=1e-12)
+    np.testing.assert_array_equal(A.residual_rms_norm(np.zeros((2, 16)), g, 1e-6, residual=r[:2]), r[:2])
+
+
+def test_attention_block_zero_output_projection_is_identity_and_matches_steps():
+    """W_o = 0 makes the sublayer x -> x + post_norm(0) = x; otherwise the block
+    equals its steps composed by hand."""
+    rng = np.random.default_rng(9)
+    B, S, dm, Hq, Hkv, D = 1, 12, 16, 2, 1, 8
+    x = rng.standard_normal((B, S, dm))
+    wq, wk, wv = (rng.standard_normal((H * D, dm)) / 4 for H in (Hq, Hkv, Hkv))
+    gi, gp, gq, gk = (1 + 0.1 * rng.standard_normal(n) for n in (dm, dm, D, D))
+    args = (Hq, Hkv, gi, gp, gq, gk, 1e-6, A.LOCAL, 4, 1e4, 1.0)
+    np.testing.assert_array_equal(A.attention_block(x, wq, wk, wv, np.zeros((dm, Hq * D)), *args), x)
+    wo = rng.standard_normal((dm, Hq * D)) / 4
+    got = A.attention_block(x, wq, wk, wv, wo, *args)
+    h = A.rms_norm(x, gi, 1e-6)
+    q, k, v = h @ wq.T, h @ wk.T, h @ wv.T
+    o = A.prefill(q.reshape(B, S, Hq, D), k.reshape(B, S, Hkv, D), v.reshape(B, S, Hkv, D), A.LOCAL, 4, 1e4, 1.0,
+                  gq, gk, 1e-6)
+    y = o.reshape(B, S, Hq * D) @ wo.T
+    np.testing.assert_allclose(got, x + A.rms_norm(y, gp, 1e-6), rtol=0, atol=1e-12)

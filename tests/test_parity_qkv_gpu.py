@@ -13,7 +13,7 @@ import pytest
 
 import oracle.attention as A
 import workloads as W
-from tests.gpu_util import assert_parity, dev_bf16, dev_f32, host
+from tests.gpu_util import assert_parity, dev_bf16, dev_f32, errors, host
 
 pytestmark = pytest.mark.gpu
 
@@ -193,3 +193,81 @@ def test_qkv_project_27b_sampled_rows():
     kn = A.qknorm_rope(rk[0], gk, W.EPS, toks, base, scale, True)  # positions = token indices
     ref[0] = kn.transpose(1, 0, 2)
     assert_proj(kh_s, ref, "khat")
+
+
+@pytest.mark.parametrize("T,n_in,n_out", [(300, 256, 384), (1, 64, 128), (1024, 128, 256)])
+def test_o_project_matches_oracle(T, n_in, n_out):
+    """Ragged token tiles, a single token, an odd number of 128-feature
+    blocks (the last tile has one), exact tiles."""
+    a = W.host_normal_bf16((1, T, n_in // 64, 64), W.seed_of(25, T, W.T_X))  # heads of 64 values
+    w = W.host_weight_bf16((n_out, n_in), W.seed_of(25, T, W.T_W))
+    y = G.o_project(dev_bf16(a), dev_bf16(w))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (1, T, n_out)
+    assert_proj(host(y), A.o_project(a, w), "y")
+
+
+def test_o_project_27b_sampled_rows():
+    """The 27B o_proj (4096 -> 5376) over 8192 tokens; the oracle projects 40
+    sampled tokens."""
+    T, Hq = 8192, 32
+    a = W.host_normal_bf16((1, T, Hq, D), W.seed_of(26, 0, W.T_X))
+    w = W.host_weight_bf16((W.D_MODEL_27B, Hq * D), W.seed_of(26, 0, W.T_W))
+    print("o_project 27B 8192 x 4096 -> 5376", flush=True)
+    y = G.o_project(dev_bf16(a), dev_bf16(w))
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([[0, 255, 256, 8191], np.random.default_rng(6).integers(0, T, 36)]))
+    ti = torch.as_tensor(toks, device="cuda")
+    assert_proj(host(y[:, ti]), A.o_project(a[:, toks], w), "y")
+
+
+@pytest.mark.parametrize("T,width,residual,gamma", [(300, 5376, True, True), (7, 1152, False, True),
+                                                    (64, 64, True, False), (3, 8192, False, False)])
+def test_rmsnorm_matches_oracle(T, width, residual, gamma):
+    x = W.bf16_round(W.host_normal_bf16((T, width), W.seed_of(27, width, W.T_X)) * 3.0)  # both sides see these bf16 values
+    r = W.host_normal_bf16((T, width), W.seed_of(27, width, W.T_Q)) if residual else None
+    g = W.host_gamma(width, W.seed_of(27, width, W.T_GK)) if gamma else None
+    out = G.rmsnorm(dev_bf16(x), dev_f32(g) if gamma else None, W.EPS, residual=dev_bf16(r) if residual else None)
+    torch.cuda.synchronize()
+    assert_proj(host(out), A.residual_rms_norm(x, g, W.EPS, residual=r), "rmsnorm")
+    if residual:  # in place into the residual stream
+        rd = dev_bf16(r)
+        G.rmsnorm(dev_bf16(x), dev_f32(g) if gamma else None, W.EPS, residual=rd, out=rd)
+        torch.cuda.synchronize()
+        assert bool(torch.equal(rd, out)), "in-place result differs"
+
+
+@pytest.mark.parametrize("kind", [A.LOCAL, A.GLOBAL])
+def test_attention_block_from_input_end_to_end(kind):
+    """The whole attention sublayer through the library: input RMSNorm, fused
+    q/k/v projection, prefill on the projected keys, o_proj, post-attention
+    RMSNorm added to the residual; against the oracle's block."""
+    B, S, dm, Hq, Hkv = 2, 500, 256, 4, 2
+    x = W.host_normal_bf16((B, S, dm), W.seed_of(28, kind, W.T_X))
+    w = W.host_weight_bf16(((Hq + 2 * Hkv) * D, dm), W.seed_of(28, kind, W.T_W))
+    wo = W.host_weight_bf16((dm, Hq * D), W.seed_of(28, kind, W.T_V))
+    gq, gk = W.host_gamma(D, W.seed_of(28, kind, W.T_GQ)), W.host_gamma(D, W.seed_of(28, kind, W.T_GK))
+    gi, gp = W.host_gamma(dm, W.seed_of(28, kind, W.T_CK)), W.host_gamma(dm, W.seed_of(28, kind, W.T_CV))
+    base, scale = (W.ROPE_BASE_LOCAL, 1.0) if kind == A.LOCAL else (W.ROPE_BASE_GLOBAL, 8.0)
+    window = 200
+    xd = dev_bf16(x)
+    h = G.rmsnorm(xd, dev_f32(gi), W.EPS)
+    q, kh, v = G.qkv_project(h, dev_bf16(w), Hq, Hkv, base, scale, dev_f32(gk), W.EPS)
+    o = G.prefill_khat(q, kh, v, kind, window, base, scale, dev_f32(gq), W.EPS)
+    y = G.o_project(o, dev_bf16(wo))
+    out = G.rmsnorm(y, dev_f32(gp), W.EPS, residual=xd)
+    torch.cuda.synchronize()
+    wq, wk, wv = _split(w, Hq, Hkv)
+    ref = A.attention_block(x, wq, wk, wv, wo, Hq, Hkv, gi, gp, gq, gk, W.EPS, kind, window, base, scale)
+    # The post-attention RMSNorm rescales the attention output (of size about
+    # 1 / sqrt(visible keys)) to unit RMS, so the attention's absolute error
+    # becomes a relative one: the gate is the relative-L2 bound (1e-2) on the
+    # sublayer's contribution out - x and on the whole output, with a loose
+    # per-element bound (10% of unit scale) against outliers.
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    xr = np.asarray(x, dtype=np.float64)
+    ec = errors(got - xr, ref - xr)
+    e = errors(got, ref)
+    assert ec["rel_l2"] <= 1e-2 and e["rel_l2"] <= 1e-2, (ec, e)
+    assert ec["max_abs"] <= 0.1, ec
