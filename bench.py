@@ -13,11 +13,13 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   * prefill_1b and decode_1b : the same two blocks at Gemma 3 1B shapes
                    (Hq=4, Hkv=1, D=256): one 32768-token sequence, and 32
                    sequences with 32767 cached positions;
-  * qkv leg      : the prefill block from the layer input instead: per
-                   layer the fused q/k/v projection of x [8192, 5376] (keys
-                   normed and rotated in its epilogue), then the flash
-                   prefill on those keys; the same projection through
-                   torch's library GEMM is timed beside it for context.
+  * qkv leg      : the prefill block as whole attention sublayers from the
+                   layer input x [8192, 5376]: per layer input RMSNorm, the
+                   fused q/k/v projection (keys normed and rotated in its
+                   epilogue), the flash prefill on those keys, o_proj and the
+                   post-attention RMSNorm added to the residual; the same
+                   q/k/v projection through torch's library GEMM is timed
+                   beside it for context.
 Beside the steps, once: the whole 62-layer 27B attention stack (52 local,
 10 global) over one 128K sequence, the prompt through chunked prefills of
 4096 tokens and then a decode loop, on per-layer caches (``schedule``).
@@ -178,6 +180,8 @@ def build_qkv_leg(torch, G, W, C):
     leg.workload = w
     leg.per_kernel = False
     leg.gemm = []
+    leg.oev = _events(torch, LAYERS)
+    leg.owork = []
     for l in range(LAYERS):
         kind = G.layer_kind(l)
         base = W.ROPE_BASE_GLOBAL if kind == G.GLOBAL else W.ROPE_BASE_LOCAL
@@ -191,18 +195,33 @@ def build_qkv_leg(torch, G, W, C):
         o = torch.empty_like(q)
         ws = torch.empty(G.prefill_workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device="cuda")
         y = torch.empty((w.B * w.S, wt.shape[0]), dtype=torch.bfloat16, device="cuda")
+        wo = W.device_normal_bf16((dm, w.Hq * w.D), W.seed_of(c, l, W.T_CK), std=(w.Hq * w.D) ** -0.5)
+        gi = torch.from_numpy(W.host_gamma(dm, W.seed_of(c, l, W.T_CV))).cuda()
+        gp = torch.from_numpy(W.host_gamma(dm, W.seed_of(c, l, W.T_SPANS))).cuda()
+        hn = torch.empty_like(x)
+        yo = torch.empty_like(x)
+        xo = torch.empty_like(x)
 
-        def call(x=x, wt=wt, gq=gq, gk=gk, q=q, kh=kh, v=v, o=o, ws=ws, kind=kind, base=base):
-            G.qkv_project(x, wt, w.Hq, w.Hkv, base, 1.0, gk, W.EPS, None, q=q, khat=kh, v=v)
+        def call(x=x, wt=wt, gq=gq, gk=gk, q=q, kh=kh, v=v, o=o, ws=ws, kind=kind, base=base, wo=wo, gi=gi, gp=gp,
+                 hn=hn, yo=yo, xo=xo, l=l):
+            G.rmsnorm(x, gi, W.EPS, out=hn)
+            G.qkv_project(hn, wt, w.Hq, w.Hkv, base, 1.0, gk, W.EPS, None, q=q, khat=kh, v=v)
             if leg.per_kernel:
-                G.set_timing_events(None, None)  # time the projection kernel only
+                G.set_timing_events(None, None)  # the projection kernel only
             G.prefill_khat(q, kh, v, kind, W.WINDOW, base, 1.0, gq, W.EPS, 0.0, None, None, None, o=o, workspace=ws)
+            if leg.per_kernel:
+                G.set_timing_events(*leg.oev[l])
+            G.o_project(o, wo, y=yo)
+            if leg.per_kernel:
+                G.set_timing_events(None, None)
+            G.rmsnorm(yo, gp, W.EPS, residual=x, out=xo)
 
         def gemm(x=x, wt=wt, y=y):
             torch.mm(x.view(w.B * w.S, dm), wt.t(), out=y)  # 2-D GEMM, y = x W^T
         leg.calls.append(call)
         leg.gemm.append(gemm)
         leg.work.append(2.0 * w.B * w.S * dm * (w.Hq + 2 * w.Hkv) * w.D)
+        leg.owork.append(2.0 * w.B * w.S * w.Hq * w.D * dm)
     return leg
 
 
@@ -399,6 +418,7 @@ def main():
     print(f"[bench] timed {args.steps} steps in {wall:.2f} s", file=sys.stderr, flush=True)
     # per-kernel durations (roofline), in steps of their own
     KK = max(3, args.steps // 2)
+    o_ms = [0.0] * LAYERS
     for s in range(KK):
         for leg in legs:
             run_leg(torch, G, leg, timed=False, per_kernel=True)
@@ -406,6 +426,8 @@ def main():
         for leg in legs:
             for l in range(LAYERS):
                 main_ms[leg.name][l] += leg.main_ev[l][0].elapsed_time(leg.main_ev[l][1])
+                if leg.name == "qkv":
+                    o_ms[l] += leg.oev[l][0].elapsed_time(leg.oev[l][1])
     print(f"[bench] {KK} steps of per-kernel timing done", file=sys.stderr, flush=True)
     gemm_ms = None
     if any(leg.name == "qkv" for leg in legs):
@@ -494,10 +516,16 @@ def main():
         out["fused_qkv"] = {
             "value": ach, "unit": "TFLOP/s", "workload": w.name + " from the layer input",
             "d_model": W.D_MODEL_27B, "tokens": w.B * w.S, "heads": [w.Hq, w.Hkv, w.Hkv],
-            "block_ms": ms, "projection_flop_per_layer": leg.work[0],
+            "block_ms": ms, "block": "per layer: input RMSNorm, fused q/k/v projection, prefill on the projected "
+                                     "keys, o_proj, post-attention RMSNorm added to the residual",
+            "projection_flop_per_layer": leg.work[0],
             "roofline": {"bound": "mfma", "kernel": "qkv_proj", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
                          "traffic": _traffic("qkv_proj.hip", "qkv_proj_27b_block"), "launch_ms": kms},
+            "o_proj": {"value": sum(leg.owork) / (sum(o_ms) / KK * 1e-3) / 1e12, "unit": "TFLOP/s",
+                       "kernel": "qkv_proj (no key/value heads)", "flop_per_layer": leg.owork[0],
+                       "frac": sum(leg.owork) / (sum(o_ms) / KK * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                       "launch_ms": [t / KK for t in o_ms]},
             "library_gemm": None if gemm_ms is None else {
                 "what": "torch.mm (library GEMM) of the same projection into one [tokens, 8192] output, "
                         "without the key norm and rotation",
