@@ -71,7 +71,9 @@ struct DecodeArgs {
 
 // Fused QKV projection (head dimension 128): W is [Hq + 2 Hkv][128][K]
 // (the q, k and v weight matrices stacked, rows = output features), x is
-// [T][K] with T = B S tokens.
+// [T][K] with T = B S tokens.  With Hkv = 0 the kernel is a plain GEMM
+// q = x W^T whose [T][Hq][128] output is a row-major [T][128 Hq] (o_proj);
+// khat, v, k_gamma and the position/rotation tables are then unused.
 struct QkvArgs {
   const uint16_t* x;      // [T][K]
   const uint16_t* w;      // [(Hq + 2 Hkv) * 128][K]
