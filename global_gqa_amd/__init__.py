@@ -259,13 +259,13 @@ def prefill_khat(q, khat, v, layer_kind: int, window: int, rope_base: float, int
 def qkv_project(x, w, Hq: int, Hkv: int, rope_base: float, interp_scale: float, k_gamma, eps: float,
                 pos0: Optional[Sequence[int]] = None, q=None, khat=None, v=None, stream=None):
     """Input projections of one layer with the key prologue fused: x
-    [B, S, d_model] bf16, w [(Hq + 2 Hkv) * 128, d_model] bf16 (Wq, Wk, Wv
-    rows stacked).  Returns (q [B, S, Hq, 128] raw, khat [B, Hkv, S, 128]
-    normed + rotated, v [B, S, Hkv, 128] raw)."""
+    [B, S, d_model] bf16, w [(Hq + 2 Hkv) * D, d_model] bf16 (Wq, Wk, Wv
+    rows stacked; D = 128 or 256 from its shape).  Returns (q [B, S, Hq, D]
+    raw, khat [B, Hkv, S, D] normed + rotated, v [B, S, Hkv, D] raw)."""
     import torch
 
     B, S, dm = x.shape
-    D = 128
+    D = w.shape[0] // (Hq + 2 * Hkv)
     _check_tensor("x", x, torch.bfloat16)
     _check_tensor("w", w, torch.bfloat16, ((Hq + 2 * Hkv) * D, dm))
     _check_tensor("k_gamma", k_gamma, torch.float32, (D,))

@@ -389,6 +389,7 @@ int g3attn_o_project(const g3_bf16* attn, const g3_bf16* w_o, g3_bf16* y, int32_
   a.K = in_features;
   a.Hq = out_features / 128;
   a.Hkv = 0;
+  a.D = 128;
   g3::Pos0Table p0t{};
   p0t.uniform = 1;
   g3::RopeTable rt{};
@@ -427,7 +428,7 @@ int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* 
                        int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, float rope_base,
                        float interp_scale, const float* k_gamma, float eps, const int32_t* pos0, void* stream) {
   g_err[0] = 0;
-  if (D != 128) return fail(G3_EUNSUPPORTED, "qkv_project supports head dim 128 only (got D=%d)", D);
+  if (D != 128 && D != 256) return fail(G3_EUNSUPPORTED, "qkv_project supports head dim 128 or 256 (got D=%d)", D);
   if (B <= 0 || S <= 0) return fail(G3_EINVAL, "B=%d and S=%d must be positive", B, S);
   if (Hq <= 0 || Hkv <= 0) return fail(G3_EINVAL, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
   if (d_model <= 0 || d_model % 64)
@@ -455,6 +456,7 @@ int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* 
   a.K = d_model;
   a.Hq = Hq;
   a.Hkv = Hkv;
+  a.D = D;
   hipStream_t st = (hipStream_t)stream;
   if (g_ev_start) hipEventRecord(g_ev_start, st);
   const hipError_t le = g3::launch_qkv_proj(a, p0t, rope_table(rope_base, interp_scale, D), st);

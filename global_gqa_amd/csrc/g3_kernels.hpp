@@ -80,9 +80,10 @@ struct QkvArgs {
   uint16_t* q;            // [T][Hq][128] raw
   uint16_t* khat;         // [B][Hkv][S][128] normed + rotated
   uint16_t* v;            // [T][Hkv][128] raw
-  const float* k_gamma;   // fp32 [128] or null (no norm)
+  const float* k_gamma;   // fp32 [D] or null (no norm)
   float eps;
   int T, S, K, Hq, Hkv;
+  int D;                  // head dimension: 128, or 256 (one head per 256-feature tile)
 };
 
 // Row RMSNorm over the model width with an optional residual add.

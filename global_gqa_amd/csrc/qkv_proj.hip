@@ -72,21 +72,29 @@ __device__ __forceinline__ void qbarrier() { asm volatile("s_waitcnt lgkmcnt(0)\
 
 __device__ __forceinline__ int qswz(int r) { return (r >> 2) & 3; }
 
-// Epilogue of one 32-token block of one head: lane (ln, h2) holds token t's
-// features n = 32 b + 8 (r / 4) + 4 h2 + r % 4 in acc[b][r], b = 0..3.
+// q or v rows of one 32-token block: lane (ln, h2) holds token t's features
+// n = 32 b + 8 (r / 4) + 4 h2 + r % 4 in acc[b][r], b = 0..3, at offset foff
+// of a head of D features.
+__device__ __forceinline__ void store_plain_rows(const QkvArgs& a, const f32x16* acc, int head, int t, int h2,
+                                                 int foff) {
+  uint16_t* dst = (head < a.Hq ? a.q + ((long long)t * a.Hq + head) * a.D
+                               : a.v + ((long long)t * a.Hkv + (head - a.Hq - a.Hkv)) * a.D) + foff;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int n = 32 * b + 8 * g4 + 4 * h2;
+      *(u32x2*)(dst + n) = u32x2{pack2(acc[b][4 * g4], acc[b][4 * g4 + 1]),
+                                 pack2(acc[b][4 * g4 + 2], acc[b][4 * g4 + 3])};
+    }
+}
+
+// Epilogue of one 32-token block at head dimension 128: lane (ln, h2) holds
+// token t's features n = 32 b + 8 (r / 4) + 4 h2 + r % 4 in acc[b][r].
 __device__ __forceinline__ void store_head_rows(const QkvArgs& a, const Pos0Table& p0t, const RopeTable& rt,
                                                 const f32x16* acc, int head, int t, int h2) {
   if (head < a.Hq || head >= a.Hq + a.Hkv) {
-    uint16_t* dst = head < a.Hq ? a.q + ((long long)t * a.Hq + head) * kQD
-                                : a.v + ((long long)t * a.Hkv + (head - a.Hq - a.Hkv)) * kQD;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int n = 32 * b + 8 * g4 + 4 * h2;
-        *(u32x2*)(dst + n) = u32x2{pack2(acc[b][4 * g4], acc[b][4 * g4 + 1]),
-                                   pack2(acc[b][4 * g4 + 2], acc[b][4 * g4 + 3])};
-      }
+    store_plain_rows(a, acc, head, t, h2, 0);
     return;
   }
   // key head: QK-RMSNorm over the 128 features, then RoPE at the token's
@@ -128,6 +136,68 @@ __device__ __forceinline__ void store_head_rows(const QkvArgs& a, const Pos0Tabl
     }
 }
 
+// Key head at head dimension 256: the tile is one head; wave w holds
+// features 128 (w & 1) .. + 127 for its 64 tokens, so the norm's sum and the
+// RoPE pairs (d, d + 128) span the two waves of a token group.  Each 32-token
+// block goes through LDS: every wave writes its sum of squares and its fp32
+// values (feature-major, 128 x 32 floats), then reads its partner's.  Called
+// by every wave of the workgroup (it holds barriers).
+__device__ __forceinline__ void store_key_rows_d256(const QkvArgs& a, const Pos0Table& p0t, const RopeTable& rt,
+                                                    f32x16 (&acc)[2][4], int head, int t0, int wave, int h2, int ln,
+                                                    float* xbuf, float* sbuf) {
+  const int wf = wave & 1, wt = wave >> 1, partner = wave ^ 1;
+  float* mine = xbuf + wave * (128 * 32);
+  const float* theirs = xbuf + partner * (128 * 32);
+  __syncthreads();  // every wave is done with the operand stages that xbuf reuses
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = t0 + 64 * wt + 32 * j + ln;
+    float ss = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = 32 * b + 8 * (r / 4) + 4 * h2 + r % 4;
+        ss += acc[j][b][r] * acc[j][b][r];
+        mine[n * 32 + ln] = acc[j][b][r];
+      }
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+      ss = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (h2 == 0) sbuf[wave * 32 + ln] = ss;
+    __syncthreads();
+    const float tot = ss + sbuf[partner * 32 + ln];
+    const float rn = a.k_gamma ? __frsqrt_rn(tot * (1.f / 256.f) + a.eps) : 1.f;
+    if (t < a.T) {
+      const int bt = t / a.S, s = t - bt * a.S;
+      const int pos = pos0_of(p0t, bt) + s;
+      uint16_t* dst = a.khat + (((long long)bt * a.Hkv + (head - a.Hq)) * a.S + s) * 256 + 128 * wf;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int n = 32 * b + 8 * g4 + 4 * h2 + e;  // pair (n, n + 128); this wave holds n + 128 wf
+            float xo = acc[j][b][4 * g4 + e] * rn, xp = theirs[n * 32 + ln] * rn;
+            if (a.k_gamma) {
+              xo *= a.k_gamma[128 * wf + n];
+              xp *= a.k_gamma[128 * (wf ^ 1) + n];
+            }
+            float sn, cs;
+            rope_sincos(pos, rt.rev[n], sn, cs);
+            y[e] = wf == 0 ? xo * cs - xp * sn : xp * sn + xo * cs;
+          }
+          const int n = 32 * b + 8 * g4 + 4 * h2;
+          *(u32x2*)(dst + n) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+        }
+    }
+    __syncthreads();  // the partner has read this block before the next one overwrites it
+  }
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(512, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, RopeTable rt) {
@@ -144,7 +214,7 @@ __global__ __launch_bounds__(512, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
   const int K = a.K;
   const int n_chunks = K / kQC;
   const int last = n_chunks - 1;
-  const int n_rows = (a.Hq + 2 * a.Hkv) * kQD;
+  const int n_rows = (a.Hq + 2 * a.Hkv) * a.D;
 
   // loads: load k = wave + 4 j (the W tile for k < 16, else the X tile)
   // fills LDS pieces P = 64 (k mod 16) + lane of its tile: row P / 4, slot
@@ -240,6 +310,20 @@ __global__ __launch_bounds__(512, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
   // released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  if (a.D == 256) {  // one head per tile, wave w holds its features 128 (w & 1) ..
+    const int head = blockIdx.y;
+    if (head >= a.Hq && head < a.Hq + a.Hkv) {
+      __shared__ float sbuf[kQWaves * 32];
+      store_key_rows_d256(a, p0t, rt, acc, head, t0, wave, h2, ln, (float*)lds, sbuf);
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = t0 + 64 * wt + 32 * j + ln;
+      if (t < a.T) store_plain_rows(a, acc[j], head, t, h2, 128 * wf);
+    }
+    return;
+  }
   const int head = blockIdx.y * 2 + wf;
   if (head >= a.Hq + 2 * a.Hkv) return;
 #pragma unroll
@@ -250,7 +334,8 @@ __global__ __launch_bounds__(512, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
 }
 
 hipError_t launch_qkv_proj(const QkvArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st) {
-  const dim3 grid((a.T + kQT - 1) / kQT, (a.Hq + 2 * a.Hkv + 1) / 2);
+  const int heads = a.Hq + 2 * a.Hkv;
+  const dim3 grid((a.T + kQT - 1) / kQT, a.D == 256 ? heads : (heads + 1) / 2);
   hipLaunchKernelGGL(qkv_proj, grid, dim3(64 * kQWaves), 0, st, a, p0t, rt);
   return hipGetLastError();
 }

@@ -133,7 +133,8 @@ size_t g3attn_prefill_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t H
  * q: [B][S][Hq][D] raw; khat: [B][Hkv][S][D] normed + rotated;
  * v: [B][S][Hkv][D] raw.  All outputs are written in full.
  * k_gamma: device fp32 [D] or NULL (no norm); pos0 as in g3attn_prefill.
- * Supported: D = 128 and d_model a multiple of 64 (else G3_EUNSUPPORTED);
+ * Supported: D = 128 or 256 and d_model a multiple of 64 (else
+ *   G3_EUNSUPPORTED);
  *   Hq + 2 Hkv <= 65535 and B*S < 2^31 - 256 (else G3_EINVAL).
  * The timing hook, when set, brackets the projection kernel. */
 int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* khat, g3_bf16* v,

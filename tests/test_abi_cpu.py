@@ -156,7 +156,7 @@ def test_qkv_project_validation_errors(L):
         a.update(kw)
         return L.g3attn_qkv_project(a["x"], a["w"], a["q"], a["kh"], a["v"], a["B"], a["S"], a["dm"], a["Hq"],
                                     a["Hkv"], a["D"], a["base"], a["scale"], None, a["eps"], a["pos0"], None)
-    assert call(D=256) == G.G3_EUNSUPPORTED and "128" in _err(L)
+    assert call(D=64) == G.G3_EUNSUPPORTED and "128 or 256" in _err(L)
     assert call(dm=100) == G.G3_EUNSUPPORTED and "multiple of 64" in _err(L)
     assert call(dm=0) == G.G3_EUNSUPPORTED
     assert call(B=0) == G.G3_EINVAL

@@ -271,3 +271,60 @@ def test_attention_block_from_input_end_to_end(kind):
     e = errors(got, ref)
     assert ec["rel_l2"] <= 1e-2 and e["rel_l2"] <= 1e-2, (ec, e)
     assert ec["max_abs"] <= 0.1, ec
+
+
+# ---------------------------------------------------------------- head dim 256 (Gemma 3 1B)
+def _proj_inputs_d(config, B, S, dm, Hq, Hkv, Dh):
+    x = W.host_normal_bf16((B, S, dm), W.seed_of(config, 0, W.T_X))
+    w = W.host_weight_bf16(((Hq + 2 * Hkv) * Dh, dm), W.seed_of(config, 0, W.T_W))
+    gq, gk = W.host_gamma(Dh, W.seed_of(config, 0, W.T_GQ)), W.host_gamma(Dh, W.seed_of(config, 0, W.T_GK))
+    return x, w, gq, gk
+
+
+@pytest.mark.parametrize("B,S,dm,Hq,Hkv,pos0,norm", [
+    (2, 300, 256, 4, 1, [0, 7000], True),      # ragged tiles over two sequences, per-sequence positions
+    (1, 1, 64, 2, 2, None, True),              # one token, one input chunk
+    (1, 513, 1152, 4, 1, None, False),         # the 1B width (1152 = 36 chunks), no norm
+])
+def test_qkv_project_d256_matches_oracle(B, S, dm, Hq, Hkv, pos0, norm):
+    """Head dimension 256: the key's RMSNorm and its RoPE pairs (d, d + 128)
+    span the two waves that hold the head's halves."""
+    Dh = 256
+    x, w, _, gk = _proj_inputs_d(29, B, S, dm, Hq, Hkv, Dh)
+    gk = gk if norm else None
+    print(f"qkv_project D=256 B={B} S={S} d_model={dm}", flush=True)
+    q, kh, v = G.qkv_project(dev_bf16(x), dev_bf16(w), Hq, Hkv, 1e6, 8.0, dev_f32(gk) if norm else None, W.EPS, pos0)
+    torch.cuda.synchronize()
+    wq, wk, wv = w[:Hq * Dh], w[Hq * Dh:(Hq + Hkv) * Dh], w[(Hq + Hkv) * Dh:]
+    rq, rk, rv = A.qkv_project(x, wq, wk, wv, Hq, Hkv)
+    assert_proj(host(q), rq, "q")
+    assert_proj(host(v), rv, "v")
+    ref = np.empty((B, Hkv, S, Dh))
+    for b in range(B):
+        pos = (0 if pos0 is None else pos0[b]) + np.arange(S)
+        ref[b] = A.qknorm_rope(rk[b], gk, W.EPS, pos, 1e6, 8.0, norm).transpose(1, 0, 2)
+    assert_proj(host(kh), ref, "khat")
+
+
+def test_attention_block_d256_from_input():
+    """A Gemma 3 1B-shaped sublayer (d_model 1152, 4 query heads and 1 kv
+    head of 256) from its input, local layer, against the oracle's block."""
+    B, S, dm, Hq, Hkv, Dh = 1, 700, 1152, 4, 1, 256
+    x, w, gq, gk = _proj_inputs_d(30, B, S, dm, Hq, Hkv, Dh)
+    wo = W.host_weight_bf16((dm, Hq * Dh), W.seed_of(30, 0, W.T_V))
+    gi, gp = W.host_gamma(dm, W.seed_of(30, 0, W.T_CK)), W.host_gamma(dm, W.seed_of(30, 0, W.T_CV))
+    window = 300
+    xd = dev_bf16(x)
+    h = G.rmsnorm(xd, dev_f32(gi), W.EPS)
+    q, kh, v = G.qkv_project(h, dev_bf16(w), Hq, Hkv, W.ROPE_BASE_LOCAL, 1.0, dev_f32(gk), W.EPS)
+    o = G.prefill_khat(q, kh, v, A.LOCAL, window, W.ROPE_BASE_LOCAL, 1.0, dev_f32(gq), W.EPS)
+    out = G.rmsnorm(G.o_project(o, dev_bf16(wo)), dev_f32(gp), W.EPS, residual=xd)
+    torch.cuda.synchronize()
+    wq, wk, wv = w[:Hq * Dh], w[Hq * Dh:(Hq + Hkv) * Dh], w[(Hq + Hkv) * Dh:]
+    ref = A.attention_block(x, wq, wk, wv, wo, Hq, Hkv, gi, gp, gq, gk, W.EPS, A.LOCAL, window, W.ROPE_BASE_LOCAL, 1.0)
+    got = host(out)
+    xr = np.asarray(x, dtype=np.float64)
+    ec, e = errors(got - xr, ref - xr), errors(got, ref)
+    assert np.all(np.isfinite(got))
+    assert ec["rel_l2"] <= 1e-2 and e["rel_l2"] <= 1e-2, (ec, e)
+    assert ec["max_abs"] <= 0.1, ec
