@@ -190,7 +190,10 @@ __device__ __forceinline__ void stream_split(const DecodeArgs& a, const float (&
 }
 
 template <int G, int D>
-__global__ __launch_bounds__(256) void decode_splitk(DecodeArgs a, RopeTable rt) {
+// Three workgroups per CU where the registers allow (G = 4: 168 VGPRs with a
+// few spills instead of 174 at two per CU, 5% faster on the 1B 32 x 32K global
+// layer, the same bits); G = 8 at D = 256 stays at two.
+__global__ __launch_bounds__(256, (D == 256 && G == 8) ? 2 : 3) void decode_splitk(DecodeArgs a, RopeTable rt) {
   constexpr int LPR = D / 8, RW = 64 / LPR, NP = D / 128;
   __shared__ float kn[D];
   __shared__ float vn[D];
