@@ -13,8 +13,8 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   * prefill_1b and decode_1b : the same two blocks at Gemma 3 1B shapes
                    (Hq=4, Hkv=1, D=256): one 32768-token sequence, and 32
                    sequences with 32767 cached positions;
-  * qkv leg      : the prefill block as whole attention sublayers from the
-                   layer input x [8192, 5376]: per layer input RMSNorm, the
+  * qkv / qkv_1b : the prefill blocks as whole attention sublayers from the
+                   layer input (27B: x [8192, 5376]; 1B: x [32768, 1152]): per layer input RMSNorm, the
                    fused q/k/v projection (keys normed and rotated in its
                    epilogue), the flash prefill on those keys, o_proj and the
                    post-attention RMSNorm added to the residual; the same
@@ -54,7 +54,7 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,chunked,prefill_1b,decode_1b,qkv")
+    ap.add_argument("--legs", default="prefill,decode,chunked,prefill_1b,decode_1b,qkv,qkv_1b")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle-on-host baseline")
     ap.add_argument("--no-schedule", action="store_true", help="skip the 62-layer 128K schedule run")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -171,11 +171,13 @@ def build_chunked_leg(torch, G, W, C):
     return leg
 
 
-def build_qkv_leg(torch, G, W, C):
-    w = W.WORKLOADS[2]
+def build_qkv_leg(torch, G, W, C, cfg=2, name="qkv", dm=None):
+    w = W.WORKLOADS[cfg]
     c = w.config
-    dm = W.D_MODEL_27B
-    leg = Leg("qkv")
+    dm = W.D_MODEL_27B if dm is None else dm
+    leg = Leg(name)
+    leg.d_model = dm
+    leg.o_ms = [0.0] * LAYERS
     leg.unit = "flop"
     leg.workload = w
     leg.per_kernel = False
@@ -387,7 +389,8 @@ def main():
     names = [s for s in args.legs.split(",") if s]
     builders = {"prefill": build_prefill_leg, "decode": build_decode_leg, "chunked": build_chunked_leg,
                 "prefill_1b": lambda *a: build_prefill_leg(*a, cfg=9, name="prefill_1b"),
-                "decode_1b": lambda *a: build_decode_leg(*a, cfg=10, name="decode_1b"), "qkv": build_qkv_leg}
+                "decode_1b": lambda *a: build_decode_leg(*a, cfg=10, name="decode_1b"), "qkv": build_qkv_leg,
+                "qkv_1b": lambda *a: build_qkv_leg(*a, cfg=9, name="qkv_1b", dm=W.D_MODEL_1B)}
     for n in names:
         leg = builders[n](torch, G, W, C)
         leg.ev_leg = _events(torch, 1)[0]
@@ -418,7 +421,6 @@ def main():
     print(f"[bench] timed {args.steps} steps in {wall:.2f} s", file=sys.stderr, flush=True)
     # per-kernel durations (roofline), in steps of their own
     KK = max(3, args.steps // 2)
-    o_ms = [0.0] * LAYERS
     for s in range(KK):
         for leg in legs:
             run_leg(torch, G, leg, timed=False, per_kernel=True)
@@ -426,11 +428,11 @@ def main():
         for leg in legs:
             for l in range(LAYERS):
                 main_ms[leg.name][l] += leg.main_ev[l][0].elapsed_time(leg.main_ev[l][1])
-                if leg.name == "qkv":
-                    o_ms[l] += leg.oev[l][0].elapsed_time(leg.oev[l][1])
+                if hasattr(leg, "oev"):
+                    leg.o_ms[l] += leg.oev[l][0].elapsed_time(leg.oev[l][1])
     print(f"[bench] {KK} steps of per-kernel timing done", file=sys.stderr, flush=True)
     gemm_ms = None
-    if any(leg.name == "qkv" for leg in legs):
+    if any(leg.name == "qkv" for leg in legs):  # the library GEMM beside the 27B projection
         leg = [x for x in legs if x.name == "qkv"][0]
         for g in leg.gemm:
             g()
@@ -507,29 +509,34 @@ def main():
         if "decode_1b" in by:
             g1["decode"] = decode_summary(by["decode_1b"])
         out["gemma3_1b"] = g1
-    if "qkv" in by:
-        leg = by["qkv"]
+    def qkv_summary(leg, tag):
         w = leg.workload
-        ms = leg_ms["qkv"] / K
-        kms = [x / KK for x in main_ms["qkv"]]
+        ms = leg_ms[leg.name] / K
+        kms = [x / KK for x in main_ms[leg.name]]
         ach = sum(leg.work) / (sum(kms) * 1e-3) / 1e12
-        out["fused_qkv"] = {
+        o_ach = sum(leg.owork) / (sum(leg.o_ms) / KK * 1e-3) / 1e12
+        return {
             "value": ach, "unit": "TFLOP/s", "workload": w.name + " from the layer input",
-            "d_model": W.D_MODEL_27B, "tokens": w.B * w.S, "heads": [w.Hq, w.Hkv, w.Hkv],
+            "d_model": leg.d_model, "tokens": w.B * w.S, "heads": [w.Hq, w.Hkv, w.Hkv], "D": w.D,
             "block_ms": ms, "block": "per layer: input RMSNorm, fused q/k/v projection, prefill on the projected "
                                      "keys, o_proj, post-attention RMSNorm added to the residual",
             "projection_flop_per_layer": leg.work[0],
             "roofline": {"bound": "mfma", "kernel": "qkv_proj", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                         "traffic": _traffic("qkv_proj.hip", "qkv_proj_27b_block"), "launch_ms": kms},
-            "o_proj": {"value": sum(leg.owork) / (sum(o_ms) / KK * 1e-3) / 1e12, "unit": "TFLOP/s",
-                       "kernel": "qkv_proj (no key/value heads)", "flop_per_layer": leg.owork[0],
-                       "frac": sum(leg.owork) / (sum(o_ms) / KK * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                       "launch_ms": [t / KK for t in o_ms]},
-            "library_gemm": None if gemm_ms is None else {
-                "what": "torch.mm (library GEMM) of the same projection into one [tokens, 8192] output, "
-                        "without the key norm and rotation",
-                "ms": gemm_ms, "TFLOPs": leg.work[0] / (gemm_ms * 1e-3) / 1e12}}
+                         "traffic": _traffic("qkv_proj.hip", f"qkv_proj_{tag}_block"), "launch_ms": kms},
+            "o_proj": {"value": o_ach, "unit": "TFLOP/s", "kernel": "qkv_proj (no key/value heads)",
+                       "flop_per_layer": leg.owork[0], "frac": o_ach / PEAK_BF16_TFLOPS,
+                       "launch_ms": [t / KK for t in leg.o_ms]}}
+
+    if "qkv" in by:
+        leg = by["qkv"]
+        out["fused_qkv"] = qkv_summary(leg, "27b")
+        out["fused_qkv"]["library_gemm"] = None if gemm_ms is None else {
+            "what": "torch.mm (library GEMM) of the same projection into one [tokens, 8192] output, "
+                    "without the key norm and rotation",
+            "ms": gemm_ms, "TFLOPs": leg.work[0] / (gemm_ms * 1e-3) / 1e12}
+    if "qkv_1b" in by:
+        out.setdefault("gemma3_1b", {})["fused_qkv"] = qkv_summary(by["qkv_1b"], "1b")
     if out["value"] is None:
         out["value"] = 0.0
     if not args.no_schedule:

@@ -36,6 +36,7 @@ import numpy as np
 
 T_Q, T_K, T_V, T_GQ, T_GK, T_CK, T_CV, T_SPANS, T_X, T_W = range(10)
 D_MODEL_27B = 5376       # hidden size in the 27B print (q_proj 5376 -> 4096)
+D_MODEL_1B = 1152        # hidden size in the 1B print (q_proj 1152 -> 1024)
 
 WINDOW = 1024            # local span (Technical Report, section 1)
 ROPE_BASE_LOCAL = 1.0e4  # Technical Report, section 2 "Long context"
