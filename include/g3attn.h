@@ -123,10 +123,11 @@ size_t g3attn_prefill_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t H
  * q = x Wq^T, k = x Wk^T, v = x Wv^T (the layer's q_proj, k_proj and v_proj,
  * linear maps without bias: "Gemma explained: What's new in Gemma 3", 27B
  * module print), then k is QK-RMSNormed with k_gamma and rotated by RoPE at
- * its absolute position (Technical Report, section 2), exactly as the
- * prologue of g3attn_prefill does, and written head-major for
- * g3attn_prefill_khat.  Accumulation is fp32; outputs are rounded to bf16
- * once (k after its norm and rotation).
+ * its absolute position (Technical Report, section 2), the same steps as
+ * the prologue of g3attn_prefill but applied to the unrounded fp32
+ * projection, and written head-major for g3attn_prefill_khat.
+ * Accumulation is fp32; outputs are rounded to bf16 once (k after its norm
+ * and rotation).
  * x: [B][S][d_model] (the normed hidden states entering the layer);
  * w: [(Hq + 2 Hkv) * D][d_model], the rows of Wq, then Wk, then Wv (each
  *   row = one output feature, head h's features at rows h*D .. h*D + D-1);
