@@ -311,7 +311,9 @@ int prefill_impl(const g3_bf16* q, const g3_bf16* k, const g3_bf16* khat_in, con
   a.is_ring = cache ? cache->is_ring : 0;
   a.has_cache = cache ? 1 : 0;
   a.local = layer_kind == G3_LOCAL;
-  a.window = layer_kind == G3_LOCAL ? window : (1 << 30);
+  // a window past any position reach means no band limit; clamped so the
+  // kernels' i + window - 1 cannot overflow
+  a.window = layer_kind == G3_LOCAL ? (window < (1 << 30) ? window : (1 << 30)) : (1 << 30);
   a.sl2 = sl2;
   const int rows = D == 256 ? g3::prefill_rows_per_wg_d256(G) : g3::prefill_rows_per_wg(G);
   a.n_qtiles = (S + rows - 1) / rows;
@@ -525,7 +527,9 @@ int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, 
   a.cap = cache->capacity;
   a.is_ring = cache->is_ring;
   a.local = layer_kind == G3_LOCAL;
-  a.window = layer_kind == G3_LOCAL ? window : (1 << 30);
+  // a window past any position reach means no band limit; clamped so the
+  // kernels' i + window - 1 cannot overflow
+  a.window = layer_kind == G3_LOCAL ? (window < (1 << 30) ? window : (1 << 30)) : (1 << 30);
   a.max_pos = max_position;
   a.n_slots = n_slots;
   a.split = split;

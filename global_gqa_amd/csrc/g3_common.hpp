@@ -70,10 +70,56 @@ __device__ __forceinline__ void rope_sincos(int pos, double rev, float& s, float
 // Map a hardware workgroup index to a logical one so that consecutive
 // logical indices land on the same XCD: the dispatcher hands workgroups to
 // the 8 XCDs round-robin, and tiles that share K/V should share an L2.
-__device__ __forceinline__ int xcd_remap(int x, int n) {
+__host__ __device__ inline int xcd_remap(int x, int n) {
   const int q = n / 8, r = n % 8;
   const int xcd = x % 8, slot = x / 8;
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// The same dispatcher dealing rounds of 8 consecutive logical indices to
+// the 8 XCDs in alternating directions (serpentine): XCD j takes index
+// 8 r + j in even rounds r and 8 r + 7 - j in odd ones (a last, partial
+// round in order).  With indices ordered heaviest first, every XCD gets an
+// even mix of heavy and light items.
+__host__ __device__ inline int xcd_serpentine(int x, int n) {
+  const int r = x / 8, j = x % 8;
+  return ((r & 1) == 0 || 8 * r + 8 > n) ? x : 8 * r + 7 - j;
+}
+
+// Prefill work items: one per (sequence, kv head) run bg < n_groups and
+// query tile, nq tiles per run.  A logical item index li is either
+// run-major (li = bg * nq + rank) or rank-major (li = rank * n_groups + bg);
+// rank 0 is the run's heaviest item (the last query tile: under the causal
+// mask it sees the most keys).
+__host__ __device__ inline void prefill_item_coords(int li, int n_groups, int nq, bool rank_major, int& bg,
+                                                    int& qt) {
+  int rank;
+  if (rank_major) {
+    rank = li / n_groups;
+    bg = li - rank * n_groups;
+  } else {
+    bg = li / nq;
+    rank = li - bg * nq;
+  }
+  qt = nq - 1 - rank;
+}
+
+// Whether a one-item-per-workgroup prefill launch orders its items
+// rank-major and deals them serpentine over the XCDs.  Run-major blocks per
+// XCD keep a run's tiles in one L2, and with a multiple of 8 runs every XCD
+// gets whole runs and equal work.  With fewer or other counts of runs, whole
+// runs cannot be spread evenly and a run's tiles differ in weight (global
+// layers: 1 to S/64 key tiles), so contiguous blocks would give one XCD the
+// heaviest tiles of a run and another its lightest: the items go out
+// rank-major (the heaviest tile of every run first) and serpentine.  Local
+// layers' items all cost about the same (window plus query tile) and keep
+// the run-major blocks for their L2 reuse.
+__host__ __device__ inline bool prefill_rank_major(bool local, int n_groups) { return !local && n_groups % 8 != 0; }
+
+// Logical item of hardware workgroup x in a launch of n = n_groups * nq
+// workgroups, one item each.
+__host__ __device__ inline int prefill_item_of_workgroup(int x, int n, bool rank_major) {
+  return rank_major ? xcd_serpentine(x, n) : xcd_remap(x, n);
 }
 
 }  // namespace g3

@@ -374,8 +374,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
 
   // The online-maximum pass only redoes the tiles the fast pass flagged.
   if (ONLINE && a.flags[li] == 0) return;
-  const int bg = li / a.n_qtiles;
-  const int qt = a.n_qtiles - 1 - (li - bg * a.n_qtiles);  // heaviest tiles first
+  int bg, qt;
+  prefill_item_coords(li, a.B * a.Hkv, a.n_qtiles, prefill_rank_major(a.local, a.B * a.Hkv), bg, qt);
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
   const int p0 = pos0_of(p0t, b);
@@ -701,13 +701,17 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
 // workgroups than items (the local layers, whose items all cost the same)
 // each workgroup runs several items back to back on its CU, and the
 // workgroups of one XCD always work on neighbouring query tiles of the same
-// kv head, which share K/V in that XCD's L2.
+// kv head, which share K/V in that XCD's L2.  With one workgroup per item
+// (the fast pass of a global layer) the item order is that of
+// prefill_item_of_workgroup.
 template <int G, bool ONLINE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW)
 void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[7 * kTileElems];
   const int n_items = a.B * a.Hkv * a.n_qtiles;
-  const int li0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int li0 = (!ONLINE && (int)gridDim.x == n_items)
+                      ? prefill_item_of_workgroup(blockIdx.x, n_items, prefill_rank_major(a.local, a.B * a.Hkv))
+                      : xcd_remap(blockIdx.x, gridDim.x);
   if (ONLINE) {
     // The online-maximum pass usually finds nothing to redo: every wave reads
     // the flags of all of this workgroup's items at once (one per lane) and

@@ -153,10 +153,12 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   const int h2 = lane >> 5;
   const int ln = lane & 31;
 
-  const int li = xcd_remap(blockIdx.x, gridDim.x);
+  // one item per workgroup, ordered by prefill_item_of_workgroup (both passes)
+  const bool rank_major = prefill_rank_major(a.local, a.B * a.Hkv);
+  const int li = prefill_item_of_workgroup(blockIdx.x, gridDim.x, rank_major);
   if (ONLINE && a.flags[li] == 0) return;
-  const int bg = li / a.n_qtiles;
-  const int qt = a.n_qtiles - 1 - (li - bg * a.n_qtiles);  // heaviest tiles first
+  int bg, qt;
+  prefill_item_coords(li, a.B * a.Hkv, a.n_qtiles, rank_major, bg, qt);
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
   // the per-sequence table is indexed at run time, which the compiler reads

@@ -16,7 +16,9 @@
  *     memory (spans, pos0) are read during the call only.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  The library allocates nothing, keeps no pointer after it
- *     returns, holds no mutable global state, and never synchronises.
+ *     returns, and never synchronises.  Its only mutable state is per calling
+ *     thread: the text of the last error, and the two timing events that
+ *     g3attn_set_timing_events installs (NULL unless a profiler sets them).
  *   - Return value: G3_OK (0) or a negative G3_E* code.  Argument errors are
  *     detected before any launch and leave every buffer untouched; the text
  *     of the last error on the calling thread is g3attn_last_error().  A
@@ -96,7 +98,8 @@ int g3attn_qknorm_rope(const g3_bf16* q_in, const g3_bf16* k_in, g3_bf16* q_out,
  * NULL for all zero).
  * Visibility of key position j to query position i (same sequence):
  *   global: j <= i, or i and j in one span;   local: that and |i - j| < window.
- * layer_kind: G3_LOCAL or G3_GLOBAL (window is ignored for global).
+ * layer_kind: G3_LOCAL or G3_GLOBAL (window is ignored for global; a local
+ *   window larger than 2^30 means no band limit).
  * softmax_scale: logit multiplier, 0 means D^-1/2; logits are not capped.
  * spans: host array of n_spans (<= 64) spans sorted by (batch, start),
  *   non-overlapping, each inside [pos0[b], pos0[b] + S); NULL if n_spans = 0.
@@ -179,10 +182,16 @@ int g3attn_prefill_khat(const g3_bf16* q, const g3_bf16* khat, const g3_bf16* v,
                         const g3_kv_cache* cache, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One decode step: each sequence b adds one token at position positions[b].
+ * Generation attends over the KV cache; local layers keep only the last
+ * window of it (span 1024), global layers all of it, which is what keeps the
+ * long-context cache small (Technical Report, abstract and section 1; the 5:1
+ * local/global interleave, section 2).  The same QK-RMSNorm and RoPE as in
+ * g3attn_qknorm_rope apply to q and to the new key.
  * q: [B][Hq][D] raw; k_new, v_new: [B][Hkv][D] raw; o: [B][Hq][D].
  * The new key is normed and rotated, written with v_new to its cache slot,
  * and the token attends to positions [0, p] (global) or
- * [max(0, p - window + 1), p] (local), itself included.
+ * [max(0, p - window + 1), p] (local), itself included.  A window larger
+ * than 2^30 means no band limit (the local layer then equals a global one).
  * positions: device int32 [B]; every entry must lie in [0, max_position]
  *   (host bound used to size the grid) and, for a linear cache, below
  *   capacity.  Entries outside that range are clamped by the kernels so no

@@ -36,10 +36,10 @@ def errors(got, ref):
     return dict(max_abs=float(d.max()), mean_abs=float(d.mean()), rel_l2=float(rel))
 
 
-def assert_parity(got, ref, what=""):
+def assert_parity(got, ref, what="", max_abs=MAX_ABS):
     e = errors(got, ref)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    assert e["max_abs"] <= MAX_ABS and e["mean_abs"] <= MEAN_ABS and e["rel_l2"] <= REL_L2, f"{what}: {e}"
+    assert e["max_abs"] <= max_abs and e["mean_abs"] <= MEAN_ABS and e["rel_l2"] <= REL_L2, f"{what}: {e}"
     return e
 
 

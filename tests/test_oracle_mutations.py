@@ -18,6 +18,7 @@ _decode_ok = A.decode
 _qkv_ok = A.qkv_project
 _oproj_ok = A.o_project
 _rres_ok = A.residual_rms_norm
+_block_ok = A.attention_block
 
 
 def rope_wrong_sign(x, positions, base, interp_scale=1.0):
@@ -129,6 +130,37 @@ def residual_dropped(x, gamma, eps, residual=None):
     return _rres_ok(x, gamma, eps)
 
 
+def _block_with(x, w_q, w_k, w_v, w_o, Hq, Hkv, gamma_in, gamma_post, q_gamma, k_gamma, eps, kind, window,
+                rope_base, interp_scale, softmax_scale=None, spans=None, pos0=None, slip=""):
+    """The oracle's sublayer with one step done wrong (``slip``)."""
+    h = x if slip == "no_input_norm" else A.residual_rms_norm(x, gamma_in, eps)
+    q, k, v = A.qkv_project(h, w_q, w_k, w_v, Hq, Hkv)
+    if slip == "k_v_swapped":
+        k, v = v, k
+    a = A.prefill(q, k, v, kind, window, rope_base, interp_scale, q_gamma, k_gamma, eps, softmax_scale, spans, pos0)
+    y = A.o_project(a, w_o)
+    res = h if slip == "residual_from_normed_input" else x
+    if slip == "no_post_norm":
+        return np.asarray(res, dtype=np.float64) + y
+    return A.residual_rms_norm(y, gamma_post, eps, residual=res)
+
+
+def block_no_input_norm(*a, **kw):
+    return _block_with(*a, slip="no_input_norm", **kw)
+
+
+def block_residual_from_normed_input(*a, **kw):
+    return _block_with(*a, slip="residual_from_normed_input", **kw)
+
+
+def block_no_post_norm(*a, **kw):
+    return _block_with(*a, slip="no_post_norm", **kw)
+
+
+def block_k_v_swapped(*a, **kw):
+    return _block_with(*a, slip="k_v_swapped", **kw)
+
+
 def _all_pins():
     out = []
     for name in dir(P):
@@ -174,6 +206,10 @@ MUTATIONS = [
     ("qkv_project", qkv_row_of_weight),
     ("o_project", o_project_heads_interleaved),
     ("residual_rms_norm", residual_dropped),
+    ("attention_block", block_no_input_norm),
+    ("attention_block", block_residual_from_normed_input),
+    ("attention_block", block_no_post_norm),
+    ("attention_block", block_k_v_swapped),
 ]
 
 

@@ -459,3 +459,63 @@ def test_attention_block_zero_output_projection_is_identity_and_matches_steps():
                   gq, gk, 1e-6)
     y = o.reshape(B, S, Hq * D) @ wo.T
     np.testing.assert_allclose(got, x + A.rms_norm(y, gp, 1e-6), rtol=0, atol=1e-12)
+
+
+def _block_inputs(rng, B, S, dm, Hq, Hkv, D):
+    x = rng.standard_normal((B, S, dm))
+    wq, wk, wv = (rng.standard_normal((H * D, dm)) / 4 for H in (Hq, Hkv, Hkv))
+    wo = rng.standard_normal((dm, Hq * D)) / 4
+    gi, gp, gq, gk = (1 + 0.3 * rng.standard_normal(n) for n in (dm, dm, D, D))
+    return x, wq, wk, wv, wo, gi, gp, gq, gk
+
+
+@pytest.mark.parametrize("kind", [A.LOCAL, A.GLOBAL])
+def test_attention_block_input_norm_makes_the_sublayer_scale_free(kind):
+    """With eps = 0 and no QK-norm, the sublayer sees x only through the input
+    RMSNorm, which is blind to the scale of x: block(c x) - c x equals
+    block(x) - x for any c > 0.  Without that norm (or with it after the
+    projections), the logits would grow like c^2 and the softmax change."""
+    rng = np.random.default_rng(21)
+    B, S, dm, Hq, Hkv, D = 2, 9, 16, 4, 2, 8
+    x, wq, wk, wv, wo, gi, gp, _, _ = _block_inputs(rng, B, S, dm, Hq, Hkv, D)
+    args = (Hq, Hkv, gi, gp, None, None, 0.0, kind, 3, 1e4, 1.0)
+    base = A.attention_block(x, wq, wk, wv, wo, *args) - x
+    for c in (0.25, 3.7):
+        got = A.attention_block(c * x, wq, wk, wv, wo, *args) - c * x
+        np.testing.assert_allclose(got, base, rtol=0, atol=1e-11)
+
+
+def test_attention_block_adds_rows_of_unit_rms():
+    """The post-attention RMSNorm makes what the sublayer adds to the residual
+    a row of mean square exactly 1 before its gamma (eps = 0):
+    mean(((block(x) - x) / gamma_post)^2) = 1 for every token."""
+    rng = np.random.default_rng(22)
+    B, S, dm, Hq, Hkv, D = 2, 7, 16, 2, 1, 8
+    x, wq, wk, wv, wo, gi, gp, gq, gk = _block_inputs(rng, B, S, dm, Hq, Hkv, D)
+    for kind in (A.LOCAL, A.GLOBAL):
+        out = A.attention_block(x, wq, wk, wv, wo, Hq, Hkv, gi, gp, gq, gk, 0.0, kind, 4, 1e6, 8.0)
+        ms = np.mean(((out - x) / gp) ** 2, axis=-1)
+        np.testing.assert_allclose(ms, 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (2, 2)])
+def test_attention_block_single_token_is_the_value_path(Hq, Hkv):
+    """A one-token sequence attends only to itself, and a softmax over one key
+    is 1, so attention returns that token's value vector (query head h gets
+    kv head h / G).  The sublayer is then
+    x + RMSNorm_post(W_o [v of each head's kv group]), v = W_v RMSNorm_in(x),
+    written out here with plain array operations; q, k, the rotation and the
+    QK-norm drop out."""
+    rng = np.random.default_rng(23)
+    dm, D, eps = 16, 8, 1e-6
+    x, wq, wk, wv, wo, gi, gp, gq, gk = _block_inputs(rng, 1, 1, dm, Hq, Hkv, D)
+    xr = x[0, 0]
+    h = xr / np.sqrt(np.mean(xr * xr) + eps) * gi
+    v = (wv @ h).reshape(Hkv, D)
+    G = Hq // Hkv
+    heads = np.concatenate([v[i // G] for i in range(Hq)])
+    y = wo @ heads
+    want = xr + y / np.sqrt(np.mean(y * y) + eps) * gp
+    for kind in (A.LOCAL, A.GLOBAL):
+        got = A.attention_block(x, wq, wk, wv, wo, Hq, Hkv, gi, gp, gq, gk, eps, kind, 1, 1e4, 1.0, pos0=[5])
+        np.testing.assert_allclose(got[0, 0], want, rtol=0, atol=1e-12)

@@ -149,7 +149,7 @@ def test_chunked_prefill_against_cache(kind, is_ring, cap, p0):
 
 
 @pytest.mark.parametrize("kind,is_ring,cap", [(A.GLOBAL, False, 5000), (A.LOCAL, True, 1024)])
-@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (2, 2)])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (2, 2), (8, 1), (4, 2)])  # G = 4, 1, 8, 2
 def test_decode_against_cache(kind, is_ring, cap, Hq, Hkv):
     B = 4
     positions = np.array([0, 700, 1023, 4097], dtype=np.int32)

@@ -116,6 +116,31 @@ def test_prefill_edge_shapes(S, window):
         assert_parity(got, ref, f"S={S} W={window} kind={kind}")
 
 
+@pytest.mark.parametrize("D", [128, 256])
+def test_local_window_past_any_reach_equals_global(D):
+    """A local layer whose window exceeds every position gap has no band
+    limit: with the largest int32 window the prefill (self-contained and
+    against a linear cache) and the decode give the global layer's bits."""
+    B, S, Hq, Hkv = 2, 700, 4, 1
+    q, k, v, gq, gk = _inputs(8, 200 + D, B, S, Hq, Hkv, D=D)
+    big = 2 ** 31 - 1
+    loc = _run_prefill(q, k, v, gq, gk, A.LOCAL, 1e4, 1.0, window=big)
+    glo = _run_prefill(q, k, v, gq, gk, A.GLOBAL, 1e4, 1.0, window=big)
+    assert np.array_equal(loc, glo), "prefill: local with an unbounded window differs from global"
+    assert_parity(loc, A.prefill(q, k, v, A.GLOBAL, W.WINDOW, 1e4, 1.0, gq, gk, W.EPS), "unbounded window")
+    cap, p = 900, 800
+    ck = W.host_normal_bf16((B, Hkv, cap, D), W.seed_of(8, 210 + D, W.T_CK))
+    cv = W.host_normal_bf16((B, Hkv, cap, D), W.seed_of(8, 210 + D, W.T_CV))
+    pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+    outs = []
+    for kind in (A.LOCAL, A.GLOBAL):
+        cache = G.KVCache(dev_bf16(ck), dev_bf16(cv), False)
+        outs.append(host(G.decode(dev_bf16(q[:, 0]), dev_bf16(k[:, 0]), dev_bf16(v[:, 0]), pos, p, cache, kind, big,
+                                  1e4, 1.0, dev_f32(gq), dev_f32(gk), W.EPS)))
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1]), "decode: local with an unbounded window differs from global"
+
+
 def test_prefill_span_covering_whole_sequence_and_edges():
     B, S, Hq, Hkv = 3, 300, 2, 1
     q, k, v, gq, gk = _inputs(8, 99, B, S, Hq, Hkv)

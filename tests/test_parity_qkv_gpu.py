@@ -36,6 +36,33 @@ def assert_proj(got, ref, what=""):
     assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} out of tolerance; worst {np.abs(got - ref)[bad].max()}"
 
 
+# Max-abs gate on the attention output inside a sublayer.  The attention's
+# own bar is 2e-2 on unit-scale bf16 inputs; here its inputs are the
+# projections of the bf16-rounded normed input, each rounded to bf16 once,
+# while the oracle projects exactly.  That rounding reaches o undamped where
+# a row sees few keys (row 0 sees only itself, so o = v): two roundings of
+# 2^-9 relative on values up to |v| ~ 5 add ~2e-2, hence 4e-2.  Mean-abs and
+# relative L2 keep the attention bar.
+MAX_ABS_SUBLAYER_O = 4e-2
+
+
+def assert_sublayer(got, ref, x):
+    """Gate for a whole sublayer's output x + RMSNorm_post(o_proj(attention)).
+
+    The post-attention RMSNorm rescales the attention's o_proj output (of
+    size about 1 / sqrt(visible keys)) to unit RMS, so the attention's error,
+    absolute and within the attention bar on o, comes out relative to unit
+    scale in what the sublayer adds: relative L2 <= 1e-2 on that contribution
+    and on the whole output, mean-abs <= 8e-3 (0.8 of the L2 bound, the ratio
+    of mean-abs to RMS for normal errors) and max-abs <= 0.1 against
+    outliers."""
+    assert np.all(np.isfinite(got)), "non-finite sublayer output"
+    xr = np.asarray(x, dtype=np.float64)
+    ec, e = errors(got - xr, ref - xr), errors(got, ref)
+    assert ec["rel_l2"] <= 1e-2 and e["rel_l2"] <= 1e-2, (ec, e)
+    assert ec["mean_abs"] <= 8e-3 and ec["max_abs"] <= 0.1, ec
+
+
 def _proj_inputs(config, B, S, dm, Hq, Hkv):
     x = W.host_normal_bf16((B, S, dm), W.seed_of(config, 0, W.T_X))
     w = W.host_weight_bf16(((Hq + 2 * Hkv) * D, dm), W.seed_of(config, 0, W.T_W))
@@ -259,18 +286,11 @@ def test_attention_block_from_input_end_to_end(kind):
     torch.cuda.synchronize()
     wq, wk, wv = _split(w, Hq, Hkv)
     ref = A.attention_block(x, wq, wk, wv, wo, Hq, Hkv, gi, gp, gq, gk, W.EPS, kind, window, base, scale)
-    # The post-attention RMSNorm rescales the attention output (of size about
-    # 1 / sqrt(visible keys)) to unit RMS, so the attention's absolute error
-    # becomes a relative one: the gate is the relative-L2 bound (1e-2) on the
-    # sublayer's contribution out - x and on the whole output, with a loose
-    # per-element bound (10% of unit scale) against outliers.
-    got = host(out)
-    assert np.all(np.isfinite(got))
-    xr = np.asarray(x, dtype=np.float64)
-    ec = errors(got - xr, ref - xr)
-    e = errors(got, ref)
-    assert ec["rel_l2"] <= 1e-2 and e["rel_l2"] <= 1e-2, (ec, e)
-    assert ec["max_abs"] <= 0.1, ec
+    # the attention output itself, at the bar every attention output meets
+    rq, rk, rv = A.qkv_project(A.residual_rms_norm(x, gi, W.EPS), wq, wk, wv, Hq, Hkv)
+    assert_parity(host(o), A.prefill(rq, rk, rv, kind, window, base, scale, gq, gk, W.EPS), "attention output",
+                  max_abs=MAX_ABS_SUBLAYER_O)
+    assert_sublayer(host(out), ref, x)
 
 
 # ---------------------------------------------------------------- head dim 256 (Gemma 3 1B)
@@ -322,9 +342,7 @@ def test_attention_block_d256_from_input():
     torch.cuda.synchronize()
     wq, wk, wv = w[:Hq * Dh], w[Hq * Dh:(Hq + Hkv) * Dh], w[(Hq + Hkv) * Dh:]
     ref = A.attention_block(x, wq, wk, wv, wo, Hq, Hkv, gi, gp, gq, gk, W.EPS, A.LOCAL, window, W.ROPE_BASE_LOCAL, 1.0)
-    got = host(out)
-    xr = np.asarray(x, dtype=np.float64)
-    ec, e = errors(got - xr, ref - xr), errors(got, ref)
-    assert np.all(np.isfinite(got))
-    assert ec["rel_l2"] <= 1e-2 and e["rel_l2"] <= 1e-2, (ec, e)
-    assert ec["max_abs"] <= 0.1, ec
+    rq, rk, rv = A.qkv_project(A.residual_rms_norm(x, gi, W.EPS), wq, wk, wv, Hq, Hkv)
+    assert_parity(host(o), A.prefill(rq, rk, rv, A.LOCAL, window, W.ROPE_BASE_LOCAL, 1.0, gq, gk, W.EPS),
+                  "attention output", max_abs=MAX_ABS_SUBLAYER_O)
+    assert_sublayer(host(out), ref, x)
