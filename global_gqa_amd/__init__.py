@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
     L.g3attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, ctypes.POINTER(KVCacheC), i32, i32, f32,
                                 f32, vp, vp, f32, f32, vp, sz, vp]
     L.g3attn_decode.restype = ctypes.c_int
+    L.g3attn_decode_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, ctypes.POINTER(KVCacheC), i32,
+                                        i32, f32, f32, vp, vp, f32, f32, vp]
+    L.g3attn_decode_noalloc.restype = ctypes.c_int
     L.g3attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(KVCacheC)]
     L.g3attn_decode_workspace_size.restype = sz
     L.g3attn_last_error.argtypes = []
@@ -353,6 +356,36 @@ def decode(q, k_new, v_new, positions, max_position: int, cache: KVCache, layer_
                                int(max_position), ctypes.byref(cc), int(layer_kind), int(window), float(rope_base),
                                float(interp_scale), _ptr(q_gamma), _ptr(k_gamma), float(eps), float(softmax_scale),
                                workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
+
+
+DECODE_NOALLOC_MAX_BYTES = 16 << 20  # G3_DECODE_NOALLOC_MAX_BYTES
+
+
+def decode_noalloc(q, k_new, v_new, positions, max_position: int, cache: KVCache, layer_kind: int, window: int,
+                   rope_base: float, interp_scale: float, q_gamma, k_gamma, eps: float, softmax_scale: float = 0.0,
+                   o=None, stream=None):
+    """decode() through g3attn_decode_noalloc: no workspace; the split-K
+    partials go to the library's static per-GPU array (calls overlapping on
+    one GPU race).  With ``o`` given, the call allocates nothing."""
+    import torch
+
+    B, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    _check_tensor("q", q, torch.bfloat16)
+    _check_tensor("k_new", k_new, torch.bfloat16, (B, Hkv, D))
+    _check_tensor("v_new", v_new, torch.bfloat16, (B, Hkv, D))
+    _check_tensor("positions", positions, torch.int32, (B,))
+    _check_tensor("q_gamma", q_gamma, torch.float32, (D,))
+    _check_tensor("k_gamma", k_gamma, torch.float32, (D,))
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("o", o, torch.bfloat16, q.shape)
+    cc = cache.c()
+    _check(lib().g3attn_decode_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(o), B, Hq, Hkv, D, _ptr(positions),
+                                       int(max_position), ctypes.byref(cc), int(layer_kind), int(window),
+                                       float(rope_base), float(interp_scale), _ptr(q_gamma), _ptr(k_gamma),
+                                       float(eps), float(softmax_scale), _stream(stream)))
     return o
 
 

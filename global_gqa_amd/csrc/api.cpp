@@ -474,11 +474,17 @@ size_t g3attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
   return decode_ws(B, Hq, D, decode_chunks(decode_slots(cache, max_position), B, Hkv));
 }
 
-int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, g3_bf16* o, int32_t B, int32_t Hq,
-                  int32_t Hkv, int32_t D, const int32_t* positions, int32_t max_position, const g3_kv_cache* cache,
-                  int32_t layer_kind, int32_t window, float rope_base, float interp_scale, const float* q_gamma,
-                  const float* k_gamma, float eps, float softmax_scale, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode step.  With noalloc the split-K partials go to the library's
+// static per-GPU array instead of the caller's workspace.
+int decode_impl(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, g3_bf16* o, int32_t B, int32_t Hq,
+                int32_t Hkv, int32_t D, const int32_t* positions, int32_t max_position, const g3_kv_cache* cache,
+                int32_t layer_kind, int32_t window, float rope_base, float interp_scale, const float* q_gamma,
+                const float* k_gamma, float eps, float softmax_scale, void* workspace, size_t workspace_bytes,
+                bool noalloc, void* stream) {
   g_err[0] = 0;
   if (int e = check_heads(Hq, Hkv, D)) return e;
   if (B <= 0) return fail(G3_EINVAL, "B=%d must be positive", B);
@@ -504,10 +510,23 @@ int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, 
   const int split = decode_split(n_slots, B, Hkv);
   const int n_chunks = decode_chunks(n_slots, B, Hkv);
   const size_t need = decode_ws(B, Hq, D, n_chunks);
-  if (!workspace || workspace_bytes < need)
-    return fail(G3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(G3_EINVAL, "workspace must be 256-byte aligned");
+  if (noalloc) {
+    if (need > g3::kDecodeScratchBytes)
+      return fail(G3_EWORKSPACE,
+                  "decode needs %zu bytes of split-K scratch, above the %zu bytes of the static array behind "
+                  "g3attn_decode_noalloc; call g3attn_decode with a workspace",
+                  need, g3::kDecodeScratchBytes);
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(G3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(G3_EINVAL, "workspace must be 256-byte aligned");
+  }
   if ((long long)B * Hkv > 65535) return fail(G3_EUNSUPPORTED, "B*Hkv=%lld exceeds 65535", (long long)B * Hkv);
+  if (noalloc) {
+    if (hipError_t e = g3::decode_scratch(&workspace))
+      return fail(G3_EHIP, "static decode scratch unavailable on this device: %s", hipGetErrorString(e));
+  }
 
   g3::DecodeArgs a{};
   a.q = q;
@@ -540,6 +559,28 @@ int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, 
                                        g_ev_start, g_ev_stop))
     return fail(G3_EHIP, "decode launch failed: %s", hipGetErrorString(e));
   return G3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, g3_bf16* o, int32_t B, int32_t Hq,
+                  int32_t Hkv, int32_t D, const int32_t* positions, int32_t max_position, const g3_kv_cache* cache,
+                  int32_t layer_kind, int32_t window, float rope_base, float interp_scale, const float* q_gamma,
+                  const float* k_gamma, float eps, float softmax_scale, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return decode_impl(q, k_new, v_new, o, B, Hq, Hkv, D, positions, max_position, cache, layer_kind, window, rope_base,
+                     interp_scale, q_gamma, k_gamma, eps, softmax_scale, workspace, workspace_bytes, false, stream);
+}
+
+int g3attn_decode_noalloc(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, g3_bf16* o, int32_t B,
+                          int32_t Hq, int32_t Hkv, int32_t D, const int32_t* positions, int32_t max_position,
+                          const g3_kv_cache* cache, int32_t layer_kind, int32_t window, float rope_base,
+                          float interp_scale, const float* q_gamma, const float* k_gamma, float eps,
+                          float softmax_scale, void* stream) {
+  return decode_impl(q, k_new, v_new, o, B, Hq, Hkv, D, positions, max_position, cache, layer_kind, window, rope_base,
+                     interp_scale, q_gamma, k_gamma, eps, softmax_scale, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -18,6 +18,8 @@
 #include "g3_common.hpp"
 #include "g3_kernels.hpp"
 
+#include <mutex>
+
 namespace g3 {
 
 namespace {
@@ -388,6 +390,28 @@ __global__ __launch_bounds__(1024) void decode_combine(DecodeArgs a) {
   }
   const float o = d2 > 0.f ? n2 / d2 : 0.f;
   a.o[(long long)h * D + d] = (uint16_t)(pack2(o, 0.f) & 0xffffu);
+}
+
+// Split-K partials of the decode entry point that allocates nothing: one
+// fixed array per GPU the library runs on, held until the process ends and
+// shared by every such call on that GPU.  On the host the name `scratch`
+// is only a stand-in for the device array (passing it to a kernel would
+// fault); decode_scratch() looks up each device's own address of it once,
+// with that device current, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  static hipError_t err[kMaxDevices];
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] { err[dev] = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch)); });
+  if (err[dev] != hipSuccess) return err[dev];
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start,

@@ -97,6 +97,9 @@ struct NormArgs {
 };
 
 constexpr int kDecodeChunk = 256;  // granularity of split-K decode splits (slots)
+// Size of the per-GPU static array behind the decode entry point that
+// allocates nothing (G3_DECODE_NOALLOC_MAX_BYTES in the C header).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
 
 hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st);
 hipError_t launch_append_chunk(const AppendArgs& a, const Pos0Table& p0t, hipStream_t st);
@@ -110,6 +113,9 @@ hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t st);
 int rmsnorm_max_width();
 hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
+// Address, on the current device, of the static split-K partials array
+// (kDecodeScratchBytes); looked up once per device.
+hipError_t decode_scratch(void** ptr);
 
 // Flash prefill: waves per workgroup (each wave owns 32 query rows).
 #ifndef G3_PREFILL_WAVES

@@ -209,6 +209,29 @@ int g3attn_decode(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, 
 size_t g3attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                     int32_t max_position, const g3_kv_cache* cache);
 
+/* Size of the static per-GPU scratch array behind g3attn_decode_noalloc. */
+#define G3_DECODE_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+
+/* g3attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Every argument means what it means for g3attn_decode; there is no
+ * workspace argument: the split-K partials go to a static device array of
+ * G3_DECODE_NOALLOC_MAX_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call there).  The call allocates nothing and issues no memset
+ * (nothing in the array needs to start at zero).
+ * A call whose partials would need more than G3_DECODE_NOALLOC_MAX_BYTES
+ * (g3attn_decode_workspace_size tells) returns G3_EWORKSPACE before any
+ * launch.  All calls on one GPU share the array: calls that overlap in time
+ * on that GPU (different streams, or host threads without ordering) race and
+ * give undefined results; calls ordered on one stream are safe. */
+int g3attn_decode_noalloc(const g3_bf16* q, const g3_bf16* k_new, const g3_bf16* v_new, g3_bf16* o,
+                          int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                          const int32_t* positions, int32_t max_position, const g3_kv_cache* cache,
+                          int32_t layer_kind, int32_t window, float rope_base, float interp_scale,
+                          const float* q_gamma, const float* k_gamma, float eps, float softmax_scale,
+                          void* stream);
+
 /* Text of the last error on this thread ("" if none); valid until the next
  * call on this thread. */
 const char* g3attn_last_error(void);

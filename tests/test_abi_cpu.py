@@ -207,3 +207,23 @@ def test_o_project_and_rmsnorm_validation_errors(L):
     assert norm(eps=-1.0) == G.G3_EINVAL
     assert norm(out=None) == G.G3_EINVAL
     assert norm(res=FAKE + 4) == G.G3_EINVAL and "aligned" in _err(L)
+
+
+def test_decode_noalloc_rejects_partials_beyond_its_static_array(L):
+    """g3attn_decode_noalloc refuses, before any launch, a call whose split-K
+    partials exceed its static array (512 sequences x 32 heads x 9 splits of
+    a 32K cache: 76.7 MB > 16 MiB); the limit is the header's."""
+    src = open(os.path.join(ROOT, "include", "g3attn.h")).read()
+    assert re.search(r"#define G3_DECODE_NOALLOC_MAX_BYTES \(\(size_t\)16 << 20\)", src)
+    assert G.DECODE_NOALLOC_MAX_BYTES == 16 << 20
+    lin = G.KVCacheC(FAKE, FAKE, 40000, 0)
+    need = L.g3attn_decode_workspace_size(512, 32, 16, 128, 32768, ctypes.byref(lin))
+    assert need == 512 * 32 * 9 * 130 * 4 > G.DECODE_NOALLOC_MAX_BYTES
+    rc = L.g3attn_decode_noalloc(FAKE, FAKE, FAKE, FAKE, 512, 32, 16, 128, FAKE, 32768, ctypes.byref(lin), G.GLOBAL,
+                                 1024, 1e6, 1.0, None, None, 1e-6, 0.0, None)
+    assert rc == G.G3_EWORKSPACE
+    assert b"static array" in L.g3attn_last_error()
+    # argument errors are still reported as for g3attn_decode
+    rc = L.g3attn_decode_noalloc(FAKE, FAKE, FAKE, FAKE, 1, 3, 2, 128, FAKE, 10, ctypes.byref(lin), G.GLOBAL, 1024,
+                                 1e6, 1.0, None, None, 1e-6, 0.0, None)
+    assert rc == G.G3_EINVAL
