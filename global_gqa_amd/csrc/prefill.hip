@@ -369,6 +369,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int h2 = lane >> 5;
   const int ln = lane & 31;
 
@@ -378,7 +379,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   prefill_item_coords(li, a.B * a.Hkv, a.n_qtiles, prefill_rank_major(a.local, a.B * a.Hkv), bg, qt);
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
-  const int p0 = pos0_of(p0t, b);
+  // the per-sequence table is indexed at run time: keep the (uniform) result scalar
+  const int p0 = __builtin_amdgcn_readfirstlane(pos0_of(p0t, b));
   const int chunk_end = p0 + a.S;
   const int kmin_avail = a.has_cache ? (a.is_ring ? max(0, p0 - a.cap) : 0) : p0;
   const int qbase = p0 + qt * WP;  // first query position of the workgroup
@@ -426,7 +428,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   // instructions: lane L of instruction i lands on row 8w + 4i + L/16, chunk
   // position L % 16, so it fetches logical chunk (L % 16) ^ swz(row).  Keys
   // that do not exist read a zero row, so their p v terms vanish.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int dma_r = lane >> 4;
   const uint16_t* khat_bg = a.khat + ((long long)b * a.Hkv + g) * a.S * kD;
   const uint16_t* v_bg = a.v + ((long long)b * a.S * a.Hkv + g) * kD;
@@ -476,6 +477,29 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
       }
       const uint16_t* dst = (is_v ? lds_v(vbuf) : lds_k(kbuf)) + (8 * wave_u + 4 * i) * kD;
       dma16(src + col, lds_addr_of(dst));
+    }
+  };
+
+  // Items whose every key tile lies inside the chunk (a self-contained prompt
+  // of whole tiles) load each tile from two running bases with per-lane
+  // offsets fixed for the item: no per-tile choice of source.
+  // The lane offsets are recomputed per tile from an opaque copy of the lane
+  // index: held across the loop they would not fit next to O, Q and S.
+  const bool chunk_only = t_begin >= 0 && p0 + (t_begin + n_t) * kBN <= chunk_end;
+  auto dma_tile_chunk = [&](int t, int kbuf, int vbuf) {
+    const uint16_t* kb = khat_bg + (long long)t * kBN * kD;
+    const uint16_t* vb = v_bg + (long long)t * kBN * vstride;
+    int lo = lane;
+    asm volatile("" : "+v"(lo));
+    const int r = lo >> 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = k & 1;
+      const bool is_v = k >= 2;
+      const int col = ((lo & 15) ^ ((r << 2) | ((2 * wave_u + i) & 3))) * 8;
+      const int row = 8 * wave_u + 4 * i + r;
+      const uint16_t* dst = (is_v ? lds_v(vbuf) : lds_k(kbuf)) + (8 * wave_u + 4 * i) * kD;
+      dma16s(is_v ? vb : kb, 2u * (uint32_t)(row * (is_v ? vstride : kD) + col), lds_addr_of(dst));
     }
   };
 
@@ -576,8 +600,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   // MFMA pipe and the VALU are busy at the same time instead of in turn.
   //   group A (waves 0..NW/2-1): half 1 PV(t-1) + QK(t), half 2 softmax(t)
   //   group B (waves NW/2..NW-1): half 1 softmax(t-1),   half 2 PV(t-1) + QK(t)
-  auto run = [&](auto grp_b_tag) {
+  auto run = [&](auto grp_b_tag, auto chunk_only_tag) {
     constexpr bool GB = decltype(grp_b_tag)::value;
+    constexpr bool CHUNK_ONLY = decltype(chunk_only_tag)::value;
     f32x16 s[2];
     bf16x8 pb[4];
     bool have_p = false;  // pb holds p of the previous tile, PV still to do
@@ -597,7 +622,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
       // barrier only tile t+1's loads must have landed.
       const bool fetch = it + 2 < n_t;
       auto prefetch = [&]() {
-        if (fetch) dma_tile(t + 2, (it + 2) % 3, (it + 2) & 3);
+        if (fetch) {
+          if (CHUNK_ONLY)
+            dma_tile_chunk(t + 2, (it + 2) % 3, (it + 2) & 3);
+          else
+            dma_tile(t + 2, (it + 2) % 3, (it + 2) & 3);
+        }
       };
       auto no_dma = [](int) {};
       if (!GB) {
@@ -646,10 +676,17 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
     barrier_lds();
     if (have_p) gemm_half<true, false>(lds_v(vprev), lds_k(0), ad, pb, qreg, s, ws, [](int) {});
   };
-  if (__builtin_amdgcn_readfirstlane(tid >> 6) >= NW / 2)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
+  if (wave_u >= NW / 2) {
+    if (chunk_only)
+      run(std::true_type{}, std::true_type{});
+    else
+      run(std::true_type{}, std::false_type{});
+  } else {
+    if (chunk_only)
+      run(std::false_type{}, std::true_type{});
+    else
+      run(std::false_type{}, std::false_type{});
+  }
 
   // Fast pass (ONLINE = false): QK-RMSNorm bounds every logit by
   // scale * D * max|gamma_q| * max|gamma_k|, so for sane gammas the softmax
