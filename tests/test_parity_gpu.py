@@ -270,6 +270,85 @@ def test_decode_against_cache(kind, is_ring, cap, Hq, Hkv):
     assert_rowwise_bf16(host(cache.k), rck, "cache k after decode append")
 
 
+# A cache slot never written (a fresh allocation past a sequence's end) may hold
+# NaN.  Rows the token cannot see get probability 0, and 0 * NaN must not reach
+# the sums: the kernels drop such rows' values, not only their weights.
+_BF16_NAN = float("nan")
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (256, 4, 1)])
+@pytest.mark.parametrize("kind,is_ring,cap", [(A.GLOBAL, False, 5000), (A.LOCAL, True, 1024), (A.LOCAL, False, 5000)])
+def test_decode_ignores_nan_in_unwritten_slots(kind, is_ring, cap, D, Hq, Hkv):
+    B = 4
+    positions = np.array([3, 700, 1500, 4097], dtype=np.int32)
+    base, scale = _kind_params(kind, 8.0)
+    seed = 7000 + D + 10 * kind + int(is_ring)
+    ck = W.host_normal_bf16((B, Hkv, cap, D), seed)
+    cv = W.host_normal_bf16((B, Hkv, cap, D), seed + 1)
+    for b, p in enumerate(positions):
+        if p + 1 < cap:  # slots past p were never written (for a ring only while p < capacity)
+            ck[b, :, p + 1:] = _BF16_NAN
+            cv[b, :, p + 1:] = _BF16_NAN
+    q = W.host_normal_bf16((B, Hq, D), seed + 2)
+    kn = W.host_normal_bf16((B, Hkv, D), seed + 3)
+    vn = W.host_normal_bf16((B, Hkv, D), seed + 4)
+    gq, gk = W.host_gamma(D, 5), W.host_gamma(D, 6)
+    cache = G.KVCache(dev_bf16(ck), dev_bf16(cv), is_ring)
+    o = G.decode(dev_bf16(q), dev_bf16(kn), dev_bf16(vn), torch.from_numpy(positions).cuda(), int(positions.max()),
+                 cache, kind, W.WINDOW, base, scale, dev_f32(gq), dev_f32(gk), W.EPS)
+    torch.cuda.synchronize()
+    ref, _, _ = A.decode(q, kn, vn, ck, cv, is_ring, positions, kind, W.WINDOW, base, scale, gq, gk, W.EPS)
+    assert_parity(host(o), ref, f"decode over NaN-filled unwritten slots kind={kind} ring={is_ring} D={D}")
+
+
+@pytest.mark.parametrize("kind,is_ring,cap,p0,Stot", [(A.GLOBAL, False, 3000, 1500, 2600),
+                                                      (A.LOCAL, True, 1024, 300, 1000),
+                                                      (A.LOCAL, False, 3000, 1500, 2600)])
+def test_chunked_prefill_ignores_nan_in_unwritten_slots(kind, is_ring, cap, p0, Stot):
+    B, Hq, Hkv = 1, 4, 2
+    q, k, v, gq, gk = _inputs(4, kind, B, Stot, Hq, Hkv)
+    base, scale = _kind_params(kind, 8.0)
+    ck, cv = _fill_cache_host(k, v, gk, cap, is_ring, base, scale, p0)
+    written = min(p0, cap) if is_ring else p0
+    ck[:, :, written:] = _BF16_NAN
+    cv[:, :, written:] = _BF16_NAN
+    cache = G.KVCache(dev_bf16(ck), dev_bf16(cv), is_ring)
+    o = G.prefill(dev_bf16(q[:, p0:]), dev_bf16(k[:, p0:]), dev_bf16(v[:, p0:]), kind, W.WINDOW, base, scale,
+                  dev_f32(gq), dev_f32(gk), W.EPS, 0.0, None, [p0], cache)
+    torch.cuda.synchronize()
+    ref, _, _ = A.prefill_chunk(q[:, p0:], k[:, p0:], v[:, p0:], ck, cv, is_ring, kind, W.WINDOW, base, scale,
+                                gq, gk, W.EPS, pos0=[p0])
+    assert_parity(host(o), ref, f"chunk over NaN-filled unwritten slots kind={kind} ring={is_ring}")
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (256, 4, 1)])
+@pytest.mark.parametrize("kind,is_ring,cap", [(A.GLOBAL, False, 2000), (A.LOCAL, True, 1024)])
+def test_decode_online_max_fallback(kind, is_ring, cap, D, Hq, Hkv):
+    """Sequence 1's logits leave the fast pass's exponent range, so its splits
+    are streamed again with a running maximum; sequence 0 stays on the fast
+    pass.  As in the prefill's fallback test the logits are exact on the GPU:
+    no QK-norm, integer-valued q and keys, scale * log2(e) = 4, and rotation
+    angles below 1e-6 rad."""
+    B = 2
+    rng = np.random.default_rng(23 + D)
+    positions = np.array([1500, 1500], dtype=np.int32)
+    ck = np.round(rng.standard_normal((B, Hkv, cap, D))).astype(np.float32)
+    cv = W.host_normal_bf16((B, Hkv, cap, D), 24 + D)
+    q = np.round(rng.standard_normal((B, Hq, D))).astype(np.float32)
+    kn = np.round(rng.standard_normal((B, Hkv, D))).astype(np.float32)
+    vn = W.host_normal_bf16((B, Hkv, D), 25 + D)
+    q[0] *= 1.0 / 64  # dyadic: still exact; keeps sequence 0 on the fast pass
+    sm = 4.0 / np.log2(np.e)
+    base = W.ROPE_BASE_LOCAL if kind == A.LOCAL else W.ROPE_BASE_GLOBAL
+    cache = G.KVCache(dev_bf16(ck), dev_bf16(cv), is_ring)
+    o = G.decode(dev_bf16(q), dev_bf16(kn), dev_bf16(vn), torch.from_numpy(positions).cuda(), int(positions.max()),
+                 cache, kind, W.WINDOW, base, 1e9, None, None, W.EPS, sm)
+    torch.cuda.synchronize()
+    ref, _, _ = A.decode(q, kn, vn, ck, cv, is_ring, positions, kind, W.WINDOW, base, 1e9, None, None, W.EPS, sm)
+    assert_parity(host(o)[0], ref[0], "sequence 0 (fast pass)")
+    assert_parity(host(o)[1], ref[1], "sequence 1 (running maximum)")
+
+
 def test_decode_deterministic_and_matches_prefill_last_row():
     """Decode of token p equals row p of a self-contained prefill whose first
     p tokens were written to the cache by a chunked prefill."""
