@@ -70,6 +70,7 @@ def _parse():
     ap.add_argument("--legs", default=DEFAULT_LEGS)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle-on-host baseline")
     ap.add_argument("--no-schedule", action="store_true", help="skip the 62-layer 128K schedule run")
+    ap.add_argument("--no-probes", action="store_true", help="skip the measured MFMA / HBM ceilings")
     ap.add_argument("--kernel-events", choices=("timed", "separate"), default="timed",
                     help="record the per-kernel events inside the timed steps (default) or in steps of their own")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -497,6 +498,37 @@ def _stats(xs):
     return {"median": statistics.median(xs), "mean": statistics.fmean(xs), "min": min(xs), "max": max(xs)}
 
 
+def measured_ceilings():
+    """The roofline probes' measured ceilings on this card: dense bf16 MFMA
+    (32x32x16 chains in every wave, 2 waves per SIMD) with the shader clock it
+    ran at, and the HBM read rate over 2 GiB."""
+    from global_gqa_amd import probes
+
+    m = probes.mfma_ceiling()
+    h = probes.hbm_read_ceiling()
+    return {"mfma_bf16": {"tflops": m["tflops"], "frac_of_published": m["tflops"] / PEAK_BF16_TFLOPS,
+                          "clock_ghz": m["clock_ghz"], "what": "v_mfma_f32_32x32x16_bf16 chains only, "
+                          f"{m['workgroups']} workgroups x 4 waves, {m['mfma_per_wave']} MFMAs per wave, best of 5"},
+            "hbm_read": {"gbps": h["gbps"], "frac_of_published": h["gbps"] / PEAK_HBM_GBPS,
+                         "what": f"16-byte non-temporal loads over {h['bytes'] >> 20} MiB, best of 5 per pattern, "
+                                 f"best pattern: {h['best']['pattern']} x {h['best']['workgroups']} workgroups",
+                         "runs": h["runs"]}}
+
+
+def add_ceiling_fractions(node, ceil):
+    """Every roofline block also states its rate against the measured
+    ceiling of its bound (the published peak stays its `peak`)."""
+    if isinstance(node, dict):
+        r = node.get("roofline")
+        if isinstance(r, dict) and r.get("achieved") is not None:
+            c = ceil["mfma_bf16"]["tflops"] if r.get("bound") == "mfma" else ceil["hbm_read"]["gbps"]
+            r["ceiling_measured"] = c
+            r["frac_of_ceiling"] = r["achieved"] / c
+        for k, v in node.items():
+            if k != "roofline":
+                add_ceiling_fractions(v, ceil)
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -684,6 +716,10 @@ def main():
         out.setdefault("gemma3_1b", {})["fused_qkv"] = qkv_summary(by["qkv_1b"], "1b")
     if out["value"] is None:
         out["value"] = 0.0
+    if not args.no_probes:
+        print("[bench] roofline probes...", file=sys.stderr, flush=True)
+        out["ceilings"] = measured_ceilings()
+        add_ceiling_fractions(out, out["ceilings"])
     if not args.no_schedule:
         print("[bench] 62-layer 128K schedule...", file=sys.stderr, flush=True)
         out["schedule_27b_128k"] = run_schedule(torch, G, W, C)

@@ -15,6 +15,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libg3attn.so")
+# The roofline probes (measured MFMA and HBM ceilings) are a library of their
+# own: measurement support, not part of the attention interface.
+PROBE_SRC = "roofline_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libg3probe.so")
 
 SOURCES = ["api.cpp", "qknorm_rope.hip", "prefill.hip", "prefill_d256.hip", "decode.hip", "qkv_proj.hip", "rmsnorm.hip"]
 ARCH = "gfx950"
@@ -52,8 +56,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    pobj = _compile(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, pobj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -227,3 +227,19 @@ def test_decode_noalloc_rejects_partials_beyond_its_static_array(L):
     rc = L.g3attn_decode_noalloc(FAKE, FAKE, FAKE, FAKE, 1, 3, 2, 128, FAKE, 10, ctypes.byref(lin), G.GLOBAL, 1024,
                                  1e6, 1.0, None, None, 1e-6, 0.0, None)
     assert rc == G.G3_EINVAL
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The roofline probes' library loads and checks its arguments before any
+    device work (no GPU needed for these calls)."""
+    from global_gqa_amd import probes
+
+    if not os.path.exists(probes.PROBE_LIB_PATH):
+        pytest.skip("libg3probe.so not built")
+    P = probes._probe_lib()
+    d = ctypes.c_double()
+    assert P.g3probe_mfma(0, 10, 1, ctypes.byref(d), ctypes.byref(d), ctypes.byref(d)) == -1
+    assert P.g3probe_mfma(4, 10, 1, None, ctypes.byref(d), ctypes.byref(d)) == -1
+    assert P.g3probe_stream(None, 1 << 20, 4, 1, 0, ctypes.byref(d), ctypes.byref(d)) == -1
+    assert P.g3probe_stream(ctypes.c_void_p(16), 8, 4, 1, 0, ctypes.byref(d), ctypes.byref(d)) == -1
+    assert P.g3probe_stream(ctypes.c_void_p(16), 48, 4, 1, 1, ctypes.byref(d), ctypes.byref(d)) == -1
