@@ -105,7 +105,7 @@ hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, const Rop
 hipError_t launch_append_chunk(const AppendArgs& a, const Pos0Table& p0t, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt, const RopeTable& rt,
                           int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
-// Head dimension 256 (Gemma 3 1B): 4 waves x 32 query rows per workgroup.
+// Head dimension 256 (Gemma 3 1B): 8 waves x 32 query rows per workgroup.
 hipError_t launch_prefill_d256(const PrefillArgs& a, const Pos0Table& p0t, const SpanTable& spt,
                                const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_qkv_proj(const QkvArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st);

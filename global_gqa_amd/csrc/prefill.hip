@@ -29,6 +29,7 @@
 //     heaviest (most keys) tiles first.
 #include "g3_common.hpp"
 #include "g3_kernels.hpp"
+#include "prefill_common.hpp"
 
 #include <type_traits>
 
@@ -65,15 +66,6 @@ __device__ __forceinline__ int wave_max_i(int x) {
   return x;
 }
 
-// Value of lane l ^ 32 combined with this lane's: max / sum.
-__device__ __forceinline__ float xhalf_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xhalf_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Orders this wave's LDS writes before its later LDS reads by other lanes of
 // the same wave (LDS instructions of one wave execute in order).
@@ -83,10 +75,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Workgroup barrier that waits only for this wave's LDS operations: tile
-// loads still in flight from global memory into LDS keep flying (a
-// __syncthreads() would wait for every outstanding memory operation).
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // All but this wave's `newer` most recent global->LDS tile loads (0 or 4)
 // have landed; loads complete in issue order.
 __device__ __forceinline__ void wait_tile_loads_but(int newer) {
@@ -96,60 +84,12 @@ __device__ __forceinline__ void wait_tile_loads_but(int newer) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// One 16-byte global -> LDS load per lane (global_load_lds_dwordx4): lane L
-// writes LDS bytes [lds_addr + 16 L, +16), lds_addr taken from M0.  Written
-// as inline asm rather than the builtin so the compiler does not treat every
-// later LDS read as dependent on it (it cannot tell the tile buffers apart
-// and would wait for all loads in flight); the kernel orders these loads
-// itself with wait_tile_loads_but() before the barrier that publishes a tile.
-// M0 is declared clobbered (the compiler re-sets it if it ever needs it).
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(src), "s"(lds_addr)
-      : "m0");
-}
-// The same with a wave-uniform base in SGPRs and a 32-bit per-lane byte
-// offset: fewer per-lane address operands, no 64-bit address arithmetic.
-__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(off), "s"(base), "s"(lds_addr)
-      : "m0");
-}
 __device__ __forceinline__ uint32_t lds_addr_of(const uint16_t* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)p);
 }
 
-// A zero K/V row: the source of tile rows whose key does not exist.
-__device__ __attribute__((aligned(256))) uint16_t g_zero_row[128] = {0};
 
-__device__ __forceinline__ int floor_div64(int x) { return x >= 0 ? x / 64 : -((63 - x) / 64); }
 
-// Visible key range of query position i (inclusive), or lo > hi if none.
-struct RowRange {
-  int lo, hi;
-};
-__device__ __forceinline__ RowRange row_range(int i, int b, int kmin_avail, const PrefillArgs& a,
-                                              const SpanTable& spt) {
-  int hi = i;
-  for (int s = 0; s < spt.n; ++s) {
-    const Span sp = spt.s[s];
-    if (sp.batch == b && sp.start <= i && i < sp.end) hi = max(hi, sp.end - 1);
-  }
-  int lo = kmin_avail;
-  if (a.local) {
-    lo = max(lo, i - a.window + 1);
-    hi = min(hi, i + a.window - 1);
-  }
-  return RowRange{lo, hi};
-}
 
 // Per-wave running state of the flash loop (one query row per lane).
 struct WaveState {
@@ -410,8 +350,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   const int wg_last = min(qbase + WP, chunk_end) - 1;
   const RowRange wg_first_r = row_range(qbase, b, kmin_avail, a, spt);
   const RowRange wg_last_r = row_range(wg_last, b, kmin_avail, a, spt);
-  const int t_begin = floor_div64(wg_first_r.lo - p0);
-  const int t_end = floor_div64(wg_last_r.hi - p0);  // inclusive
+  const int t_begin = floor_div<64>(wg_first_r.lo - p0);
+  const int t_end = floor_div<64>(wg_last_r.hi - p0);  // inclusive
   const int n_t = t_end - t_begin + 1;
   int w_lo_min = 0x7fffffff, w_hi_max = -0x7fffffff, w_lo_max = 0x7fffffff, w_hi_min = -0x7fffffff;
   if (wbase < chunk_end) {

@@ -30,6 +30,7 @@
 //     the same flagged second pass (ONLINE = true) as the D = 128 kernel.
 #include "g3_common.hpp"
 #include "g3_kernels.hpp"
+#include "prefill_common.hpp"
 
 namespace g3 {
 
@@ -54,18 +55,6 @@ constexpr int kAhead = G3_D256_AHEAD;         // matrix-half operands read this 
 
 static_assert(kNW == 8, "two waves per SIMD");
 
-__device__ __forceinline__ float xhalf_sum256(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xhalf_max256(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// Barrier that waits only for this wave's LDS operations (not for global
-// loads still in flight).
-__device__ __forceinline__ void barrier_lds256() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_loads256() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most one tile's loads of this wave (4 or 5) are in flight.
 __device__ __forceinline__ void wait_loads256_but(int n) {
@@ -75,56 +64,6 @@ __device__ __forceinline__ void wait_loads256_but(int n) {
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
 }
 __device__ __forceinline__ void fence256() { __builtin_amdgcn_sched_barrier(0); }
-
-// One 16-byte global -> LDS load per lane: lane L writes LDS bytes
-// [lds_addr + 16 L, +16) (global_load_lds_dwordx4, address in M0, declared
-// clobbered).
-__device__ __forceinline__ void dma16_256(const void* src, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(src), "s"(lds_addr)
-      : "m0");
-}
-
-// The same with a wave-uniform base in SGPRs and a 32-bit per-lane byte
-// offset (half the per-lane address operands of the 64-bit form).
-__device__ __forceinline__ void dma16s_256(const void* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(off), "s"(base), "s"(lds_addr)
-      : "m0");
-}
-
-// A zero K/V row: the source of tile rows whose key does not exist and of
-// pad positions.
-__device__ __attribute__((aligned(256))) uint16_t g_zero_row256[kDh] = {0};
-
-__device__ __forceinline__ int floor_div32(int x) { return x >= 0 ? x / 32 : -((31 - x) / 32); }
-
-struct Range256 {
-  int lo, hi;
-};
-// Visible key range of query position i (inclusive), or lo > hi if none.
-__device__ __forceinline__ Range256 row_range256(int i, int b, int kmin_avail, const PrefillArgs& a,
-                                                 const SpanTable& spt) {
-  int hi = i;
-  for (int s = 0; s < spt.n; ++s) {
-    const Span sp = spt.s[s];
-    if (sp.batch == b && sp.start <= i && i < sp.end) hi = max(hi, sp.end - 1);
-  }
-  int lo = kmin_avail;
-  if (a.local) {
-    lo = max(lo, i - a.window + 1);
-    hi = min(hi, i + a.window - 1);
-  }
-  return Range256{lo, hi};
-}
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
@@ -171,14 +110,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
 
   // key tiles of the workgroup (lo(i), hi(i) are non-decreasing in i)
   const int wg_last = min(qbase + WP, chunk_end) - 1;
-  const Range256 wf = row_range256(qbase, b, kmin_avail, a, spt);
-  const Range256 wl = row_range256(wg_last, b, kmin_avail, a, spt);
-  const int t_begin = floor_div32(wf.lo - p0);
-  const int n_t = floor_div32(wl.hi - p0) - t_begin + 1;
+  const RowRange wf = row_range(qbase, b, kmin_avail, a, spt);
+  const RowRange wl = row_range(wg_last, b, kmin_avail, a, spt);
+  const int t_begin = floor_div<32>(wf.lo - p0);
+  const int n_t = floor_div<32>(wl.hi - p0) - t_begin + 1;
   int w_lo_max = 0x7fffffff, w_hi_min = -0x7fffffff;
   if (wbase < chunk_end) {
-    w_hi_min = __builtin_amdgcn_readfirstlane(row_range256(wbase, b, kmin_avail, a, spt).hi);
-    w_lo_max = __builtin_amdgcn_readfirstlane(row_range256(min(wbase + P, chunk_end) - 1, b, kmin_avail, a, spt).lo);
+    w_hi_min = __builtin_amdgcn_readfirstlane(row_range(wbase, b, kmin_avail, a, spt).hi);
+    w_lo_max = __builtin_amdgcn_readfirstlane(row_range(min(wbase + P, chunk_end) - 1, b, kmin_avail, a, spt).lo);
   }
 
   // ---- tile loader.  Load k (0..34) of a tile writes the 64 16-byte pieces
@@ -231,7 +170,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
           const uint32_t code = *(const lds_u32*)(pc + 4 * (j * 64 + lane_o));
           const bool is_v = k >= kKLoads;
           const uint32_t off = 2u * ((code >> 16) * (uint32_t)(is_v ? vs : kDh) + (code & 0xffffu));
-          dma16s_256(is_v ? vb : kb, off, dst0 + (is_v ? kKBytes + 1024 * (k - kKLoads) : 1024 * k));
+          dma16s(is_v ? vb : kb, off, dst0 + (is_v ? kKBytes + 1024 * (k - kKLoads) : 1024 * k));
         }
       }
       return;
@@ -249,7 +188,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
         const int col = is_v ? n - row * kVRow : n - row * kKRow;
         const bool data = row < kBNh && col < 32;
         const int jj = ts + row;
-        const uint16_t* src = g_zero_row256;
+        const uint16_t* src = g_zero_row;
         if (data) {
           if (jj >= p0 && jj < chunk_end) {
             src = (is_v ? v_bg + (long long)(jj - p0) * vstride : khat_bg + (long long)(jj - p0) * kDh) + 8 * col;
@@ -258,7 +197,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
             src = (is_v ? cv_bg : ck_bg) + sl * kDh + 8 * col;
           }
         }
-        dma16_256(src, dst0 + (is_v ? kKBytes : 0) + 1024 * kk);
+        dma16(src, dst0 + (is_v ? kKBytes : 0) + 1024 * kk);
       }
     }
   };
@@ -295,9 +234,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
     u32x4 w[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s) w[s] = *(const u32x4*)(src + 16 * s);
-    if (a.q_gamma && wave_u == 0) dma16_256(a.q_gamma + 4 * lane, (uint32_t)(uintptr_t)(lds_char*)s_gamma);
+    if (a.q_gamma && wave_u == 0) dma16(a.q_gamma + 4 * lane, (uint32_t)(uintptr_t)(lds_char*)s_gamma);
     wait_loads256();
-    barrier_lds256();  // tiles 0 and 1, the zero V region and q_gamma are in LDS
+    barrier_lds();  // tiles 0 and 1, the zero V region and q_gamma are in LDS
     float rn = a.sl2;
     if (a.q_gamma) {
       float ss = 0.f;
@@ -305,7 +244,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
       for (int s = 0; s < 16; ++s)
 #pragma unroll
         for (int e = 0; e < 4; ++e) ss += bf_lo(w[s][e]) * bf_lo(w[s][e]) + bf_hi(w[s][e]) * bf_hi(w[s][e]);
-      ss = xhalf_sum256(ss);
+      ss = xhalf_sum(ss);
       rn *= rsqrtf(ss * (1.f / kDh) + a.eps);
     }
 #pragma unroll
@@ -410,7 +349,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
       const int rp = wbase + lnl % P;
       int row_lo = 0x7fffffff, row_hi = -0x7fffffff;
       if (rp < chunk_end) {
-        const Range256 rr = row_range256(rp, b, kmin_avail, a, spt);
+        const RowRange rr = row_range(rp, b, kmin_avail, a, spt);
         row_lo = rr.lo;
         row_hi = rr.hi;
       }
@@ -425,7 +364,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
       float mx = NEG_INF;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = xhalf_max256(mx);
+      mx = xhalf_max(mx);
       const float m_new = fmaxf(m_run, mx);
       off = (m_new == NEG_INF) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - off);
@@ -476,13 +415,13 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
         __builtin_amdgcn_s_setprio(1);
         mfma_half(std::true_type{}, vs, ks, pb, s);
         __builtin_amdgcn_s_setprio(0);
-        barrier_lds256();
+        barrier_lds();
         softmax(s, ts, full, pb);
         if (fetch) dma_tile(t + 2, (it + 2) & (kNB - 1));
       } else {
         softmax(s, s_ts, s_full, pb);
         if (fetch) dma_tile(t + 2, (it + 2) & (kNB - 1));
-        barrier_lds256();
+        barrier_lds();
         __builtin_amdgcn_s_setprio(1);
         mfma_half(std::true_type{}, vs, ks, pb, s);
         __builtin_amdgcn_s_setprio(0);
@@ -493,11 +432,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
         wait_loads256_but(n_my_loads);
       else
         wait_loads256();
-      barrier_lds256();
+      barrier_lds();
     }
     // drain: PV of the last tile (group B first runs its softmax)
     if (GB) softmax(s, s_ts, s_full, pb);
-    barrier_lds256();
+    barrier_lds();
     mfma_half(std::false_type{}, (n_t + kNB - 1) & (kNB - 1), 0, pb, s);
   };
   if (wave_u >= kNW / 2)
@@ -508,7 +447,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   // Fast pass: a workgroup with a row whose sum leaves [2^-64, 2^64] (extreme
   // gammas, no norm, foreign cache contents) stores nothing and raises its
   // flag; the ONLINE launch redoes it with the running maximum.
-  const float lt = xhalf_sum256(l_run);
+  const float lt = xhalf_sum(l_run);
   const int le = lane_opaque();
   const int hge = (le & 31) / P, h2e = le >> 5;
   const int row_pos_e = wbase + (le & 31) % P;

@@ -1,11 +1,12 @@
 // QK-RMSNorm + RoPE prologue and the KV-cache append used by chunked prefill.
 //
-// Norm: x / sqrt(mean(x^2) + eps) * gamma over the head dimension (Gemma 3
+// Norm: x / sqrt(mean(x^2) + eps) * gamma over the head dimension D (Gemma 3
 // Technical Report, section 2: QK-norm replaces soft-capping; "Gemma
-// explained" 27B module print: RMSNorm((128,), eps=1e-06)).  RoPE: pairs
-// (x_k, x_{k+64}) rotated by (p / s) * base^(-2k/128) (Technical Report,
-// section 2 "Long context": base 10k local / 1M global, linear position
-// interpolation on the global layers).  Memory bound: one read and one write
+// explained" module prints: RMSNorm over the head dimension, eps=1e-06; D is
+// 128 for the 27B model, 256 for the 1B one).  RoPE: pairs (x_k, x_{k+D/2})
+// rotated by (p / s) * base^(-2k/D) (Technical Report, section 2 "Long
+// context": base 10k local / 1M global, linear position interpolation on the
+// global layers).  Memory bound: one read and one write
 // of each head row (256 bytes at D = 128, 512 at D = 256).
 #include "g3_common.hpp"
 #include "g3_kernels.hpp"
