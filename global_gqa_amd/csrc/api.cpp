@@ -95,7 +95,10 @@ int decode_slots(const g3_kv_cache* c, int32_t max_position) {
 // With fewer pairs than that a one-unit split can leave most CUs idle (the
 // 1B model's 32 sequences x 1 kv head: 128 workgroups on a 1024-slot ring,
 // each latency-bound), so the split halves, down to 64 slots, until the grid
-// has about 1024 workgroups.
+// has about one workgroup per CU.  More, shorter splits cost more than they
+// give: every workgroup adds to the dispatch and its prologue and merge are
+// fixed costs (the 1B ring: 256 workgroups of 128 slots 15.9 us per layer,
+// 512 of 64 slots 17.2 us).
 int decode_split(int n_slots, int32_t B, int32_t Hkv) {
   const int n_units = (n_slots + g3::kDecodeChunk - 1) / g3::kDecodeChunk;
   const long long pairs = (long long)B * Hkv;
@@ -105,7 +108,7 @@ int decode_split(int n_slots, int32_t B, int32_t Hkv) {
   if (k < 1) k = 1;
   if (k > 16) k = 16;
   int split = (int)k * g3::kDecodeChunk;
-  while (split > 64 && (long long)((n_slots + split - 1) / split) * pairs < 1024) split /= 2;
+  while (split > 64 && (long long)((n_slots + split - 1) / split) * pairs < 256) split /= 2;
   return split;
 }
 int decode_chunks(int n_slots, int32_t B, int32_t Hkv) {
