@@ -101,10 +101,17 @@ def _ptr(t) -> Optional[int]:
 
 
 def _stream(stream) -> int:
+    """The HIP stream to launch on: ``stream``, else torch's current stream
+    of the current device (read as a raw handle where torch offers it: that
+    skips building a Stream object, a few microseconds per call)."""
     import torch
 
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(torch._C._cuda_getDevice())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _check_tensor(name, t, dtype, shape=None):
