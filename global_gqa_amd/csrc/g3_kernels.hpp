@@ -22,6 +22,10 @@ struct RowsArgs {
   int D;                  // head dimension (128 or 256)
 };
 
+// Heads of one token each K1 lane group normalises and rotates (their
+// rotation angles are the same, so sin/cos are computed once per group).
+constexpr int kRopeHeadsPerGroup = 4;
+
 struct AppendArgs {
   const uint16_t* khat;   // [B][Hkv][S][D]
   const uint16_t* v;      // [B][S][Hkv][D]

@@ -15,11 +15,16 @@ namespace g3 {
 
 // D/16 lanes per head row (8 at D = 128, 16 at D = 256); lane j owns dims
 // [8 j, 8 j + 8) and [D/2 + 8 j, D/2 + 8 j + 8), one 16-byte load and store
-// per half, so every rotation pair (k, k + D/2) stays inside one lane.
+// per half, so every rotation pair (k, k + D/2) stays inside one lane.  A lane
+// group takes one token and HB of its heads: the rotation angles depend on
+// the position only, so their sin/cos (fp64 reduction, two transcendentals
+// per pair) are computed once for the HB heads, and the HB rows' loads are
+// all in flight before the first is used.
 template <int D, bool NORM>
 __global__ __launch_bounds__(256) void qknorm_rope_rows(RowsArgs a, Pos0Table p0t, RopeTable rt) {
   constexpr int LPR = D / 16;     // lanes per row
-  constexpr int RPB = 256 / LPR;  // rows per workgroup pass
+  constexpr int RPB = 256 / LPR;  // lane groups per workgroup
+  constexpr int HB = kRopeHeadsPerGroup;
   const int j = threadIdx.x % LPR;
   double rev[8];
 #pragma unroll
@@ -30,52 +35,65 @@ __global__ __launch_bounds__(256) void qknorm_rope_rows(RowsArgs a, Pos0Table p0
     gam[i] = NORM ? a.gamma[8 * j + i] : 1.f;
     gam[8 + i] = NORM ? a.gamma[D / 2 + 8 * j + i] : 1.f;
   }
-  const long long n_rows = (long long)a.T * a.H;
+  const int nhb = (a.H + HB - 1) / HB;  // head blocks per token
+  const long long n_groups = (long long)a.T * nhb;
   const long long stride = (long long)gridDim.x * RPB;
-  for (long long R = (long long)blockIdx.x * RPB + threadIdx.x / LPR; R < n_rows; R += stride) {
-    const long long t = R / a.H;
-    const int h = (int)(R - t * a.H);
+  for (long long X = (long long)blockIdx.x * RPB + threadIdx.x / LPR; X < n_groups; X += stride) {
+    const long long t = X / nhb;
+    const int h0 = (int)(X - t * nhb) * HB;
     const int bt = (int)(t / a.S);
     const int st = (int)(t - (long long)bt * a.S);
     const int pos = a.positions ? a.positions[t] : pos0_of(p0t, bt) + st;
-    const uint16_t* src = a.in + R * D;
-    const u32x4 lo = *(const u32x4*)(src + 8 * j);
-    const u32x4 hi = *(const u32x4*)(src + D / 2 + 8 * j);
-    float x[16];
+    // rows past the last head re-read the last one (in bounds, never stored)
+    u32x4 lo[HB], hi[HB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf_lo(lo[e]);
-      x[2 * e + 1] = bf_hi(lo[e]);
-      x[8 + 2 * e] = bf_lo(hi[e]);
-      x[8 + 2 * e + 1] = bf_hi(hi[e]);
+    for (int u = 0; u < HB; ++u) {
+      const uint16_t* src = a.in + (t * a.H + min(h0 + u, a.H - 1)) * D;
+      lo[u] = *(const u32x4*)(src + 8 * j);
+      hi[u] = *(const u32x4*)(src + D / 2 + 8 * j);
     }
-    if (NORM) {
-      float ss = 0.f;
+    float sn[8], cs[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
+    for (int i = 0; i < 8; ++i) rope_sincos(pos, rev[i], sn[i], cs[i]);
 #pragma unroll
-      for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, LPR);
-      const float r = __frsqrt_rn(ss * (1.f / D) + a.eps);
+    for (int u = 0; u < HB; ++u) {
+      const int h = h0 + u;
+      if (h >= a.H) break;
+      float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = x[i] * r * gam[i];
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf_lo(lo[u][e]);
+        x[2 * e + 1] = bf_hi(lo[u][e]);
+        x[8 + 2 * e] = bf_lo(hi[u][e]);
+        x[8 + 2 * e + 1] = bf_hi(hi[u][e]);
+      }
+      if (NORM) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, LPR);
+        const float r = __frsqrt_rn(ss * (1.f / D) + a.eps);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = x[i] * r * gam[i];
+      }
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        y[i] = x[i] * cs[i] - x[8 + i] * sn[i];
+        y[8 + i] = x[i] * sn[i] + x[8 + i] * cs[i];
+      }
+      const long long R = t * a.H + h;
+      uint16_t* dst = a.out + (a.head_major ? (((long long)bt * a.H + h) * a.S + st) * D : R * D);
+      u32x4 wlo, whi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wlo[e] = pack2(y[2 * e], y[2 * e + 1]);
+        whi[e] = pack2(y[8 + 2 * e], y[8 + 2 * e + 1]);
+      }
+      *(u32x4*)(dst + 8 * j) = wlo;
+      *(u32x4*)(dst + D / 2 + 8 * j) = whi;
     }
-    float y[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float sn, cs;
-      rope_sincos(pos, rev[i], sn, cs);
-      y[i] = x[i] * cs - x[8 + i] * sn;
-      y[8 + i] = x[i] * sn + x[8 + i] * cs;
-    }
-    uint16_t* dst = a.out + (a.head_major ? (((long long)bt * a.H + h) * a.S + st) * D : R * D);
-    u32x4 wlo, whi;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      wlo[e] = pack2(y[2 * e], y[2 * e + 1]);
-      whi[e] = pack2(y[8 + 2 * e], y[8 + 2 * e + 1]);
-    }
-    *(u32x4*)(dst + 8 * j) = wlo;
-    *(u32x4*)(dst + D / 2 + 8 * j) = whi;
   }
 }
 
@@ -110,9 +128,10 @@ static int grid_for(long long work_items, int per_block) {
 }
 
 hipError_t launch_qknorm_rope(const RowsArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st) {
-  // a grid-stride loop over rows: at most 8 workgroups per CU
+  // a grid-stride loop over (token, head block) groups: at most 8 workgroups per CU
   const int rpb = 256 / (a.D / 16);
-  long long grid = ((long long)a.T * a.H + rpb - 1) / rpb;
+  const long long groups = (long long)a.T * ((a.H + kRopeHeadsPerGroup - 1) / kRopeHeadsPerGroup);
+  long long grid = (groups + rpb - 1) / rpb;
   if (grid > 2048) grid = 2048;
   if (a.D == 256) {
     if (a.gamma)
