@@ -234,14 +234,16 @@ def build_qkv_leg(torch, G, W, C, cfg=2, name="qkv", dm=None):
         wo = W.device_normal_bf16((dm, w.Hq * w.D), W.seed_of(c, l, W.T_CK), std=(w.Hq * w.D) ** -0.5)
         gi = torch.from_numpy(W.host_gamma(dm, W.seed_of(c, l, W.T_CV))).cuda()
         gp = torch.from_numpy(W.host_gamma(dm, W.seed_of(c, l, W.T_SPANS))).cuda()
-        hn = torch.empty_like(x)
+        # the input norm's gamma folded into the projection weights once (load time)
+        wf = G.fold_norm_weight(wt, gi)
+        xs = torch.empty((w.B, w.S), dtype=torch.float32, device="cuda")
         yo = torch.empty_like(x)
         xo = torch.empty_like(x)
 
-        def call(x=x, wt=wt, gq=gq, gk=gk, q=q, kh=kh, v=v, o=o, ws=ws, kind=kind, base=base, wo=wo, gi=gi, gp=gp,
-                 hn=hn, yo=yo, xo=xo, l=l):
-            G.rmsnorm(x, gi, W.EPS, out=hn)
-            G.qkv_project(hn, wt, w.Hq, w.Hkv, base, 1.0, gk, W.EPS, None, q=q, khat=kh, v=v)
+        def call(x=x, wf=wf, xs=xs, gq=gq, gk=gk, q=q, kh=kh, v=v, o=o, ws=ws, kind=kind, base=base, wo=wo, gp=gp,
+                 yo=yo, xo=xo, l=l):
+            G.rms_scale(x, W.EPS, scale=xs)
+            G.qkv_project(x, wf, w.Hq, w.Hkv, base, 1.0, gk, W.EPS, None, q=q, khat=kh, v=v, x_scale=xs)
             if leg.per_kernel:
                 G.set_timing_events(None, None)  # the projection kernel only
             G.prefill_khat(q, kh, v, kind, W.WINDOW, base, 1.0, gq, W.EPS, 0.0, None, None, None, o=o, workspace=ws)
@@ -731,8 +733,10 @@ def main():
         return {
             "value": ach, "unit": "TFLOP/s", "workload": w.name + " from the layer input",
             "d_model": leg.d_model, "tokens": w.B * w.S, "heads": [w.Hq, w.Hkv, w.Hkv], "D": w.D,
-            "block_ms": st, "block": "per layer: input RMSNorm, fused q/k/v projection, prefill on the projected "
-                                     "keys, o_proj, post-attention RMSNorm added to the residual",
+            "block_ms": st, "block": "per layer: the input RMSNorm's per-token scale (its gamma folded into the "
+                                     "projection weights once, before the timed steps), the fused q/k/v "
+                                     "projection applying that scale, prefill on the projected keys, o_proj, "
+                                     "post-attention RMSNorm added to the residual",
             "projection_flop_per_layer": leg.work[0],
             "roofline": {"bound": "mfma", "kernel": "qkv_proj", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,

@@ -58,13 +58,17 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(Span), i32, ctypes.POINTER(i32), ctypes.POINTER(KVCacheC), vp,
                                       sz, vp]
     L.g3attn_prefill_khat.restype = ctypes.c_int
-    L.g3attn_qkv_project.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp, f32,
+    L.g3attn_qkv_project.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp, f32,
                                      ctypes.POINTER(i32), vp]
     L.g3attn_qkv_project.restype = ctypes.c_int
     L.g3attn_o_project.argtypes = [vp, vp, vp, i32, i32, i32, vp]
     L.g3attn_o_project.restype = ctypes.c_int
     L.g3attn_rmsnorm.argtypes = [vp, vp, vp, f32, vp, i32, i32, vp]
     L.g3attn_rmsnorm.restype = ctypes.c_int
+    L.g3attn_rms_scale.argtypes = [vp, f32, vp, i32, i32, vp]
+    L.g3attn_rms_scale.restype = ctypes.c_int
+    L.g3attn_fold_norm_weight.argtypes = [vp, vp, vp, i32, i32, vp]
+    L.g3attn_fold_norm_weight.restype = ctypes.c_int
     L.g3attn_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.g3attn_prefill_workspace_size.restype = sz
     L.g3attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, ctypes.POINTER(KVCacheC), i32, i32, f32,
@@ -267,16 +271,22 @@ def prefill_khat(q, khat, v, layer_kind: int, window: int, rope_base: float, int
 
 
 def qkv_project(x, w, Hq: int, Hkv: int, rope_base: float, interp_scale: float, k_gamma, eps: float,
-                pos0: Optional[Sequence[int]] = None, q=None, khat=None, v=None, stream=None):
+                pos0: Optional[Sequence[int]] = None, q=None, khat=None, v=None, stream=None, x_scale=None):
     """Input projections of one layer with the key prologue fused: x
     [B, S, d_model] bf16, w [(Hq + 2 Hkv) * D, d_model] bf16 (Wq, Wk, Wv
-    rows stacked; D = 128 or 256 from its shape).  Returns (q [B, S, Hq, D]
-    raw, khat [B, Hkv, S, D] normed + rotated, v [B, S, Hkv, D] raw)."""
+    rows stacked; D = 128 or 256 from its shape).  x_scale: fp32 [B, S] (or
+    [B * S]) multiplying each token's projections (the input norm folded in:
+    raw x, x_scale = rms_scale(x), w = fold_norm_weight(w, gamma)).  Returns
+    (q [B, S, Hq, D] raw, khat [B, Hkv, S, D] normed + rotated, v [B, S, Hkv,
+    D] raw)."""
     import torch
 
     B, S, dm = x.shape
     D = w.shape[0] // (Hq + 2 * Hkv)
     _check_tensor("x", x, torch.bfloat16)
+    _check_tensor("x_scale", x_scale, torch.float32)
+    if x_scale is not None and x_scale.numel() != B * S:
+        raise ValueError(f"x_scale has {x_scale.numel()} elements, expected {B * S}")
     _check_tensor("w", w, torch.bfloat16, ((Hq + 2 * Hkv) * D, dm))
     _check_tensor("k_gamma", k_gamma, torch.float32, (D,))
     if q is None:
@@ -289,7 +299,8 @@ def qkv_project(x, w, Hq: int, Hkv: int, rope_base: float, interp_scale: float, 
     _check_tensor("khat", khat, torch.bfloat16, (B, Hkv, S, D))
     _check_tensor("v", v, torch.bfloat16, (B, S, Hkv, D))
     _, _, p0 = _spans_pos0(None, pos0, B)
-    _check(lib().g3attn_qkv_project(_ptr(x), _ptr(w), _ptr(q), _ptr(khat), _ptr(v), B, S, dm, Hq, Hkv, D,
+    _check(lib().g3attn_qkv_project(_ptr(x), _ptr(x_scale), _ptr(w), _ptr(q), _ptr(khat), _ptr(v), B, S, dm, Hq,
+                                    Hkv, D,
                                     float(rope_base), float(interp_scale), _ptr(k_gamma), float(eps), p0,
                                     _stream(stream)))
     return q, khat, v
@@ -337,6 +348,39 @@ def rmsnorm(x, gamma, eps: float, residual=None, out=None, stream=None):
                                 _stream(stream)))
     return out
 
+
+
+def rms_scale(x, eps: float, scale=None, stream=None):
+    """scale[t] = 1 / sqrt(mean(x[t]^2) + eps) over the last axis of bf16 x:
+    fp32 of shape x.shape[:-1]; the input norm's per-token factor for
+    qkv_project(..., x_scale=...)."""
+    import torch
+
+    W = x.shape[-1]
+    T = x.numel() // W
+    _check_tensor("x", x, torch.bfloat16)
+    if scale is None:
+        scale = torch.empty(tuple(x.shape[:-1]), dtype=torch.float32, device=x.device)
+    _check_tensor("scale", scale, torch.float32)
+    if scale.numel() != T:
+        raise ValueError(f"scale has {scale.numel()} elements, expected {T}")
+    _check(lib().g3attn_rms_scale(_ptr(x), float(eps), _ptr(scale), T, W, _stream(stream)))
+    return scale
+
+
+def fold_norm_weight(w, gamma, out=None, stream=None):
+    """w [rows, width] bf16 with gamma [width] fp32 folded in:
+    out[n, k] = w[n, k] * gamma[k], rounded to bf16 (out may be w)."""
+    import torch
+
+    _check_tensor("w", w, torch.bfloat16)
+    rows, width = w.shape
+    _check_tensor("gamma", gamma, torch.float32, (width,))
+    if out is None:
+        out = torch.empty_like(w)
+    _check_tensor("out", out, torch.bfloat16, w.shape)
+    _check(lib().g3attn_fold_norm_weight(_ptr(w), _ptr(gamma), _ptr(out), rows, width, _stream(stream)))
+    return out
 
 def decode(q, k_new, v_new, positions, max_position: int, cache: KVCache, layer_kind: int, window: int,
            rope_base: float, interp_scale: float, q_gamma, k_gamma, eps: float, softmax_scale: float = 0.0,

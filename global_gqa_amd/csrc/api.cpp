@@ -150,7 +150,7 @@ extern "C" {
 
 const char* g3attn_last_error(void) { return g_err; }
 
-int32_t g3attn_version(void) { return 100; }
+int32_t g3attn_version(void) { return 101; }
 
 int g3attn_set_timing_events(void* start, void* stop) {
   g_ev_start = (hipEvent_t)start;
@@ -429,9 +429,40 @@ int g3attn_rmsnorm(const g3_bf16* x, const g3_bf16* residual, const float* gamma
   return G3_OK;
 }
 
-int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* khat, g3_bf16* v, int32_t B,
-                       int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, float rope_base,
-                       float interp_scale, const float* k_gamma, float eps, const int32_t* pos0, void* stream) {
+int g3attn_rms_scale(const g3_bf16* x, float eps, float* scale, int32_t T, int32_t width, void* stream) {
+  g_err[0] = 0;
+  if (T <= 0) return fail(G3_EINVAL, "T=%d must be positive", T);
+  if (width <= 0 || width % 8 || width > (1 << 20))
+    return fail(G3_EUNSUPPORTED, "width=%d must be a positive multiple of 8 up to %d", width, 1 << 20);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(G3_EINVAL, "eps must be >= 0 (got %g)", eps);
+  if (!x || !scale) return fail(G3_EINVAL, "x and scale must be non-NULL");
+  if (!aligned16(x)) return fail(G3_EINVAL, "x must be 16-byte aligned");
+  g3::NormArgs a{};
+  a.x = x;
+  a.eps = eps;
+  a.T = T;
+  a.W = width;
+  if (hipError_t e = g3::launch_rms_scale(a, scale, (hipStream_t)stream))
+    return fail(G3_EHIP, "rms scale launch failed: %s", hipGetErrorString(e));
+  return G3_OK;
+}
+
+int g3attn_fold_norm_weight(const g3_bf16* w, const float* gamma, g3_bf16* w_out, int32_t rows, int32_t width,
+                            void* stream) {
+  g_err[0] = 0;
+  if (rows <= 0) return fail(G3_EINVAL, "rows=%d must be positive", rows);
+  if (width <= 0 || width % 8) return fail(G3_EUNSUPPORTED, "width=%d must be a positive multiple of 8", width);
+  if (!w || !gamma || !w_out) return fail(G3_EINVAL, "w, gamma and w_out must be non-NULL");
+  if (!aligned16(w) || !aligned16(w_out)) return fail(G3_EINVAL, "w and w_out must be 16-byte aligned");
+  if (hipError_t e = g3::launch_fold_gamma(w, gamma, w_out, rows, width, (hipStream_t)stream))
+    return fail(G3_EHIP, "weight fold launch failed: %s", hipGetErrorString(e));
+  return G3_OK;
+}
+
+int g3attn_qkv_project(const g3_bf16* x, const float* x_scale, const g3_bf16* w, g3_bf16* q, g3_bf16* khat,
+                       g3_bf16* v, int32_t B, int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D,
+                       float rope_base, float interp_scale, const float* k_gamma, float eps, const int32_t* pos0,
+                       void* stream) {
   g_err[0] = 0;
   if (D != 128 && D != 256) return fail(G3_EUNSUPPORTED, "qkv_project supports head dim 128 or 256 (got D=%d)", D);
   if (B <= 0 || S <= 0) return fail(G3_EINVAL, "B=%d and S=%d must be positive", B, S);
@@ -455,6 +486,7 @@ int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* 
   a.khat = khat;
   a.v = v;
   a.k_gamma = k_gamma;
+  a.x_scale = x_scale;
   a.eps = eps;
   a.T = (int)T;
   a.S = S;

@@ -85,6 +85,7 @@ struct QkvArgs {
   uint16_t* khat;         // [B][Hkv][S][128] normed + rotated
   uint16_t* v;            // [T][Hkv][128] raw
   const float* k_gamma;   // fp32 [D] or null (no norm)
+  const float* x_scale;   // fp32 [T] or null: token t's projections are multiplied by x_scale[t]
   float eps;
   int T, S, K, Hq, Hkv;
   int D;                  // head dimension: 128, or 256 (one head per 256-feature tile)
@@ -115,6 +116,12 @@ hipError_t launch_prefill_d256(const PrefillArgs& a, const Pos0Table& p0t, const
 hipError_t launch_qkv_proj(const QkvArgs& a, const Pos0Table& p0t, const RopeTable& rt, hipStream_t st);
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t st);
 int rmsnorm_max_width();
+// scale[t] = 1 / sqrt(mean(x[t]^2) + eps) for the rows of a.x (a.out, a.gamma
+// and a.residual unused).
+hipError_t launch_rms_scale(const NormArgs& a, float* scale, hipStream_t st);
+// out[n][k] = w[n][k] * gamma[k], rounded to bf16 ([rows][width]).
+hipError_t launch_fold_gamma(const uint16_t* w, const float* gamma, uint16_t* out, long long rows, int width,
+                             hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, const RopeTable& rt, int G, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
 // Address, on the current device, of the static split-K partials array

@@ -310,6 +310,20 @@ __global__ __launch_bounds__(512, 1) void qkv_proj(QkvArgs a, Pos0Table p0t, Rop
   // released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  // the input norm's per-token scale, when its gamma is folded into w: the
+  // projections of token t are x[t] w^T times x_scale[t]
+  if (a.x_scale) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = min(t0 + 64 * wt + 32 * j + ln, a.T - 1);
+      const float sc = a.x_scale[t];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][b][r] *= sc;
+    }
+  }
+
   if (a.D == 256) {  // one head per tile, wave w holds its features 128 (w & 1) ..
     const int head = blockIdx.y;
     if (head >= a.Hq && head < a.Hq + a.Hkv) {

@@ -79,12 +79,71 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_rows(NormArgs a) {
   }
 }
 
+// Only the row scale 1 / sqrt(mean(x^2) + eps), fp32: the input norm of a
+// layer whose gamma is folded into the projection weights.  One wave per row
+// (16-byte pieces, four in flight per lane); 2 bytes read per element.
+__global__ __launch_bounds__(256) void rms_scale_rows(NormArgs a, float* scale) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.T) return;
+  const int n_pieces = a.W / 8;
+  const uint16_t* src = a.x + row * a.W;
+  float ss = 0.f;
+  for (int p0 = 0; p0 < n_pieces; p0 += 4 * 64) {
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pc = p0 + lane + 64 * i;
+      v[i] = pc < n_pieces ? *(const u32x4*)(src + 8 * pc) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf_lo(v[i][e]), hi = bf_hi(v[i][e]);
+        ss += lo * lo + hi * hi;
+      }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  if (lane == 0) scale[row] = __frsqrt_rn(ss / (float)a.W + a.eps);
+}
+
+// out[n][k] = w[n][k] * gamma[k] in fp32, rounded to bf16 once; width is a
+// multiple of 8 (one 16-byte piece per thread and step).
+__global__ __launch_bounds__(256) void fold_gamma_rows(const uint16_t* w, const float* gamma, uint16_t* out,
+                                                       long long n_pieces, int width) {
+  const int ppr = width / 8;
+  for (long long x = (long long)blockIdx.x * 256 + threadIdx.x; x < n_pieces; x += (long long)gridDim.x * 256) {
+    const int k0 = 8 * (int)(x % ppr);
+    const u32x4 v = *(const u32x4*)(w + 8 * x);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack2(bf_lo(v[e]) * gamma[k0 + 2 * e], bf_hi(v[e]) * gamma[k0 + 2 * e + 1]);
+    *(u32x4*)(out + 8 * x) = o;
+  }
+}
+
 }  // namespace
 
 int rmsnorm_max_width() { return 8 * kNormPieces * kNormThreads; }
 
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(rmsnorm_rows, dim3(a.T), dim3(kNormThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_scale(const NormArgs& a, float* scale, hipStream_t st) {
+  hipLaunchKernelGGL(rms_scale_rows, dim3((a.T + 3) / 4), dim3(256), 0, st, a, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_gamma(const uint16_t* w, const float* gamma, uint16_t* out, long long rows, int width,
+                             hipStream_t st) {
+  const long long n_pieces = rows * (width / 8);
+  long long grid = (n_pieces + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(fold_gamma_rows, dim3((int)grid), dim3(256), 0, st, w, gamma, out, n_pieces, width);
   return hipGetLastError();
 }
 

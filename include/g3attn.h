@@ -131,7 +131,15 @@ size_t g3attn_prefill_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t H
  * projection, and written head-major for g3attn_prefill_khat.
  * Accumulation is fp32; outputs are rounded to bf16 once (k after its norm
  * and rotation).
- * x: [B][S][d_model] (the normed hidden states entering the layer);
+ * x: [B][S][d_model] (the normed hidden states entering the layer, or the
+ *   raw ones with x_scale below);
+ * x_scale: device fp32 [B*S] or NULL.  When given, token t's projections are
+ *   multiplied by x_scale[t] (in fp32, before rounding and before k's norm):
+ *   with x the raw hidden states, x_scale from g3attn_rms_scale and w from
+ *   g3attn_fold_norm_weight(w, input_layernorm gamma), the call computes the
+ *   projections of the normed input without the normed copy of x ever being
+ *   written (the input RMSNorm of the Technical Report, section 2, folded
+ *   into the projection: (x/rms(x) * gamma) W^T = (1/rms(x)) x (W diag(gamma))^T);
  * w: [(Hq + 2 Hkv) * D][d_model], the rows of Wq, then Wk, then Wv (each
  *   row = one output feature, head h's features at rows h*D .. h*D + D-1);
  * q: [B][S][Hq][D] raw; khat: [B][Hkv][S][D] normed + rotated;
@@ -141,10 +149,26 @@ size_t g3attn_prefill_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t H
  *   G3_EUNSUPPORTED);
  *   Hq + 2 Hkv <= 65535 and B*S < 2^31 - 256 (else G3_EINVAL).
  * The timing hook, when set, brackets the projection kernel. */
-int g3attn_qkv_project(const g3_bf16* x, const g3_bf16* w, g3_bf16* q, g3_bf16* khat, g3_bf16* v,
-                       int32_t B, int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D,
-                       float rope_base, float interp_scale, const float* k_gamma, float eps,
-                       const int32_t* pos0, void* stream);
+int g3attn_qkv_project(const g3_bf16* x, const float* x_scale, const g3_bf16* w, g3_bf16* q,
+                       g3_bf16* khat, g3_bf16* v, int32_t B, int32_t S, int32_t d_model, int32_t Hq,
+                       int32_t Hkv, int32_t D, float rope_base, float interp_scale,
+                       const float* k_gamma, float eps, const int32_t* pos0, void* stream);
+
+/* The per-token scale of the layer's input RMSNorm (Technical Report,
+ * section 2: pre-norm with RMSNorm; "Gemma explained" 27B print: RMSNorm over
+ * 5376, eps 1e-6) without the normed rows:
+ *   scale[t] = 1 / sqrt(mean(x[t]^2) + eps)      (sums in fp32)
+ * x: [T][width] bf16; scale: device fp32 [T].  For g3attn_qkv_project's
+ * x_scale.  Supported: width a multiple of 8 up to 2^20 (else
+ * G3_EUNSUPPORTED). */
+int g3attn_rms_scale(const g3_bf16* x, float eps, float* scale, int32_t T, int32_t width, void* stream);
+
+/* The input norm's gamma folded into a projection weight, once per layer at
+ * load time: w_out[n][k] = w[n][k] * gamma[k] (fp32 product, rounded to bf16
+ * once).  w, w_out: [rows][width] bf16 (w_out may alias w); gamma: device fp32
+ * [width].  Supported: width a multiple of 8 (else G3_EUNSUPPORTED). */
+int g3attn_fold_norm_weight(const g3_bf16* w, const float* gamma, g3_bf16* w_out, int32_t rows,
+                            int32_t width, void* stream);
 
 /* The layer's output projection o_proj: y = attn W_o^T ("Gemma explained:
  * What's new in Gemma 3", 27B module print: Linear 4096 -> 5376, no bias),

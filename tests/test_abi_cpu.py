@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
     assert {"g3attn_qknorm_rope", "g3attn_prefill", "g3attn_decode"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.g3attn_version() >= 100
+    assert L.g3attn_version() >= 101
 
 
 def test_workspace_sizes(L):
@@ -154,8 +154,9 @@ def test_qkv_project_validation_errors(L):
         a = dict(x=FAKE, w=FAKE, q=FAKE, kh=FAKE, v=FAKE, B=1, S=64, dm=256, Hq=4, Hkv=2, D=128, base=1e4,
                  scale=1.0, eps=1e-6, pos0=None)
         a.update(kw)
-        return L.g3attn_qkv_project(a["x"], a["w"], a["q"], a["kh"], a["v"], a["B"], a["S"], a["dm"], a["Hq"],
-                                    a["Hkv"], a["D"], a["base"], a["scale"], None, a["eps"], a["pos0"], None)
+        return L.g3attn_qkv_project(a["x"], None, a["w"], a["q"], a["kh"], a["v"], a["B"], a["S"], a["dm"],
+                                    a["Hq"], a["Hkv"], a["D"], a["base"], a["scale"], None, a["eps"], a["pos0"],
+                                    None)
     assert call(D=64) == G.G3_EUNSUPPORTED and "128 or 256" in _err(L)
     assert call(dm=100) == G.G3_EUNSUPPORTED and "multiple of 64" in _err(L)
     assert call(dm=0) == G.G3_EUNSUPPORTED
@@ -169,6 +170,18 @@ def test_qkv_project_validation_errors(L):
     assert call(Hq=70000, Hkv=1) == G.G3_EINVAL and "heads" in _err(L)
     p0 = (ctypes.c_int32 * 1)(-3)
     assert call(pos0=p0) == G.G3_EINVAL and "pos0" in _err(L)
+
+
+def test_rms_scale_and_fold_validation_errors(L):
+    assert L.g3attn_rms_scale(FAKE, 1e-6, FAKE, 0, 64, None) == G.G3_EINVAL
+    assert L.g3attn_rms_scale(FAKE, 1e-6, FAKE, 4, 12, None) == G.G3_EUNSUPPORTED and "multiple of 8" in _err(L)
+    assert L.g3attn_rms_scale(FAKE, -1.0, FAKE, 4, 64, None) == G.G3_EINVAL and "eps" in _err(L)
+    assert L.g3attn_rms_scale(FAKE, 1e-6, None, 4, 64, None) == G.G3_EINVAL and "non-NULL" in _err(L)
+    assert L.g3attn_rms_scale(FAKE + 8, 1e-6, FAKE, 4, 64, None) == G.G3_EINVAL and "aligned" in _err(L)
+    assert L.g3attn_fold_norm_weight(FAKE, FAKE, FAKE, 0, 64, None) == G.G3_EINVAL
+    assert L.g3attn_fold_norm_weight(FAKE, FAKE, FAKE, 4, 60, None) == G.G3_EUNSUPPORTED
+    assert L.g3attn_fold_norm_weight(FAKE, None, FAKE, 4, 64, None) == G.G3_EINVAL and "non-NULL" in _err(L)
+    assert L.g3attn_fold_norm_weight(FAKE, FAKE, FAKE + 8, 4, 64, None) == G.G3_EINVAL and "aligned" in _err(L)
 
 
 def test_prefill_khat_validation_errors(L):

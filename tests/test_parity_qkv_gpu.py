@@ -346,3 +346,95 @@ def test_attention_block_d256_from_input():
     assert_parity(host(o), A.prefill(rq, rk, rv, A.LOCAL, window, W.ROPE_BASE_LOCAL, 1.0, gq, gk, W.EPS),
                   "attention output", max_abs=MAX_ABS_SUBLAYER_O)
     assert_sublayer(host(out), ref, x)
+
+
+# ---------------------------------------------------------------- input norm folded into the projection
+# (x / rms(x) * gamma) W^T = (1 / rms(x)) * x (W diag(gamma))^T: the gamma goes
+# into the weight once, the per-token 1 / rms(x) is applied to the fp32
+# projections, and the normed copy of x is never written.
+@pytest.mark.parametrize("T,width", [(300, 5376), (7, 1152), (5, 8), (64, 8192)])
+def test_rms_scale_matches_definition(T, width):
+    x = W.bf16_round(W.host_normal_bf16((T, width), W.seed_of(40, width, W.T_X)) * 2.5)
+    s = G.rms_scale(dev_bf16(x), W.EPS)
+    torch.cuda.synchronize()
+    xr = x.astype(np.float64)
+    ref = 1.0 / np.sqrt(np.mean(xr * xr, axis=-1) + W.EPS)
+    # fp32 sum of squares and reciprocal square root: a few ulp of fp32
+    np.testing.assert_allclose(host(s), ref, rtol=1e-5, atol=0)
+
+
+@pytest.mark.parametrize("rows,width", [(384, 256), (3, 1152), (1, 8)])
+def test_fold_norm_weight_is_one_rounding_of_the_product(rows, width):
+    w = W.host_weight_bf16((rows, width), W.seed_of(41, width, W.T_W))
+    g = W.host_gamma(width, W.seed_of(41, width, W.T_GK))
+    out = G.fold_norm_weight(dev_bf16(w), dev_f32(g))
+    torch.cuda.synchronize()
+    ref = W.bf16_round(w.astype(np.float32) * g.astype(np.float32))
+    assert np.array_equal(host(out), ref.astype(np.float64))
+    wd = dev_bf16(w)
+    G.fold_norm_weight(wd, dev_f32(g), out=wd)  # in place
+    torch.cuda.synchronize()
+    assert np.array_equal(host(wd), ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("Dh,B,S,dm,Hq,Hkv,pos0", [
+    (128, 2, 300, 256, 4, 2, [0, 5000]),
+    (128, 1, 640, 320, 3, 1, None),
+    (256, 1, 513, 1152, 4, 1, [17]),
+])
+def test_qkv_project_with_x_scale_matches_oracle(Dh, B, S, dm, Hq, Hkv, pos0):
+    """The folded projection computes x W'^T times the token's scale: against
+    the oracle's projection of the exactly scaled x with the same folded
+    weights (W' rounded to bf16 on the host), at the projection's own gate."""
+    x = W.host_normal_bf16((B, S, dm), W.seed_of(42, Dh, W.T_X))
+    w = W.host_weight_bf16(((Hq + 2 * Hkv) * Dh, dm), W.seed_of(42, Dh, W.T_W))
+    gi = W.host_gamma(dm, W.seed_of(42, Dh, W.T_CK))
+    gk = W.host_gamma(Dh, W.seed_of(42, Dh, W.T_GK))
+    base, scale = 1e6, 8.0
+    xd = dev_bf16(x)
+    sc = G.rms_scale(xd, W.EPS)
+    wf = G.fold_norm_weight(dev_bf16(w), dev_f32(gi))
+    print(f"qkv_project x_scale D={Dh} B={B} S={S} d_model={dm}", flush=True)
+    q, kh, v = G.qkv_project(xd, wf, Hq, Hkv, base, scale, dev_f32(gk), W.EPS, pos0, x_scale=sc)
+    torch.cuda.synchronize()
+    xr = x.astype(np.float64)
+    xs = xr / np.sqrt(np.mean(xr * xr, axis=-1, keepdims=True) + W.EPS)
+    wfold = W.bf16_round(w.astype(np.float32) * gi.astype(np.float32))
+    wq, wk, wv = wfold[:Hq * Dh], wfold[Hq * Dh:(Hq + Hkv) * Dh], wfold[(Hq + Hkv) * Dh:]
+    rq, rk, rv = A.qkv_project(xs, wq, wk, wv, Hq, Hkv)
+    assert_proj(host(q), rq, "q")
+    assert_proj(host(v), rv, "v")
+    ref = np.empty((B, Hkv, S, Dh))
+    for b in range(B):
+        pos = (0 if pos0 is None else pos0[b]) + np.arange(S)
+        ref[b] = A.qknorm_rope(rk[b], gk, W.EPS, pos, base, scale, True).transpose(1, 0, 2)
+    assert_proj(host(kh), ref, "khat")
+
+
+@pytest.mark.parametrize("Dh,kind", [(128, A.LOCAL), (128, A.GLOBAL), (256, A.LOCAL)])
+def test_attention_block_folded_input_norm_end_to_end(Dh, kind):
+    """The whole sublayer with the input RMSNorm folded into the projection
+    (rms_scale + fold_norm_weight + qkv_project(x_scale)), against the
+    oracle's block, at the same gates as the unfolded sublayer."""
+    B, S, Hq, Hkv = (2, 500, 4, 2) if Dh == 128 else (1, 700, 4, 1)
+    dm = 256 if Dh == 128 else 1152
+    cfg = 43 + Dh
+    x = W.host_normal_bf16((B, S, dm), W.seed_of(cfg, kind, W.T_X))
+    w = W.host_weight_bf16(((Hq + 2 * Hkv) * Dh, dm), W.seed_of(cfg, kind, W.T_W))
+    wo = W.host_weight_bf16((dm, Hq * Dh), W.seed_of(cfg, kind, W.T_V))
+    gq, gk = W.host_gamma(Dh, W.seed_of(cfg, kind, W.T_GQ)), W.host_gamma(Dh, W.seed_of(cfg, kind, W.T_GK))
+    gi, gp = W.host_gamma(dm, W.seed_of(cfg, kind, W.T_CK)), W.host_gamma(dm, W.seed_of(cfg, kind, W.T_CV))
+    base, scale = (W.ROPE_BASE_LOCAL, 1.0) if kind == A.LOCAL else (W.ROPE_BASE_GLOBAL, 8.0)
+    window = 200
+    xd = dev_bf16(x)
+    wf = G.fold_norm_weight(dev_bf16(w), dev_f32(gi))
+    q, kh, v = G.qkv_project(xd, wf, Hq, Hkv, base, scale, dev_f32(gk), W.EPS, x_scale=G.rms_scale(xd, W.EPS))
+    o = G.prefill_khat(q, kh, v, kind, window, base, scale, dev_f32(gq), W.EPS)
+    out = G.rmsnorm(G.o_project(o, dev_bf16(wo)), dev_f32(gp), W.EPS, residual=xd)
+    torch.cuda.synchronize()
+    wq, wk, wv = w[:Hq * Dh], w[Hq * Dh:(Hq + Hkv) * Dh], w[(Hq + Hkv) * Dh:]
+    ref = A.attention_block(x, wq, wk, wv, wo, Hq, Hkv, gi, gp, gq, gk, W.EPS, kind, window, base, scale)
+    rq, rk, rv = A.qkv_project(A.residual_rms_norm(x, gi, W.EPS), wq, wk, wv, Hq, Hkv)
+    assert_parity(host(o), A.prefill(rq, rk, rv, kind, window, base, scale, gq, gk, W.EPS), "attention output",
+                  max_abs=MAX_ABS_SUBLAYER_O)
+    assert_sublayer(host(out), ref, x)
