@@ -300,8 +300,7 @@ def qkv_project(x, w, Hq: int, Hkv: int, rope_base: float, interp_scale: float, 
     _check_tensor("v", v, torch.bfloat16, (B, S, Hkv, D))
     _, _, p0 = _spans_pos0(None, pos0, B)
     _check(lib().g3attn_qkv_project(_ptr(x), _ptr(x_scale), _ptr(w), _ptr(q), _ptr(khat), _ptr(v), B, S, dm, Hq,
-                                    Hkv, D,
-                                    float(rope_base), float(interp_scale), _ptr(k_gamma), float(eps), p0,
+                                    Hkv, D, float(rope_base), float(interp_scale), _ptr(k_gamma), float(eps), p0,
                                     _stream(stream)))
     return q, khat, v
 

@@ -10,6 +10,11 @@
 // 16-byte pieces of the row in registers between the sum of squares and the
 // scaled store, so the row is read once.  HBM bound: 2 bytes read and 2
 // written per element (plus 2 read for the residual).
+//
+// The input norm can also be folded into the q/k/v projection that follows
+// it: (x / rms(x) * gamma) W^T = (1 / rms(x)) * x (W diag(gamma))^T.  For that
+// path this file also holds the row scale alone (1 / rms(x) per row, no
+// normed copy of x written) and the one-time fold of gamma into W.
 #include "g3_common.hpp"
 #include "g3_kernels.hpp"
 
@@ -134,7 +139,7 @@ hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_rms_scale(const NormArgs& a, float* scale, hipStream_t st) {
-  hipLaunchKernelGGL(rms_scale_rows, dim3((a.T + 3) / 4), dim3(256), 0, st, a, scale);
+  hipLaunchKernelGGL(rms_scale_rows, dim3((int)(((long long)a.T + 3) / 4)), dim3(256), 0, st, a, scale);
   return hipGetLastError();
 }
 

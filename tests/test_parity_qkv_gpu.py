@@ -438,3 +438,29 @@ def test_attention_block_folded_input_norm_end_to_end(Dh, kind):
     assert_parity(host(o), A.prefill(rq, rk, rv, kind, window, base, scale, gq, gk, W.EPS), "attention output",
                   max_abs=MAX_ABS_SUBLAYER_O)
     assert_sublayer(host(out), ref, x)
+
+
+def test_qkv_project_x_scale_27b_sampled_rows():
+    """The folded input norm at the 27B layer shape (8192 tokens, d_model
+    5376): raw x, the norm's gamma folded into W, the per-token scale from
+    rms_scale; the oracle projects 40 sampled tokens of the exactly normed x
+    with the host-folded weights."""
+    B, S, dm, Hq, Hkv = 1, 8192, W.D_MODEL_27B, 32, 16
+    x, w, _, gk = _proj_inputs(47, B, S, dm, Hq, Hkv)
+    gi = W.host_gamma(dm, W.seed_of(47, 0, W.T_CK))
+    base, scale = W.ROPE_BASE_LOCAL, 1.0
+    print("qkv_project x_scale 27B 8192 x 5376", flush=True)
+    xd = dev_bf16(x)
+    q, kh, v = G.qkv_project(xd, G.fold_norm_weight(dev_bf16(w), dev_f32(gi)), Hq, Hkv, base, scale, dev_f32(gk),
+                             W.EPS, x_scale=G.rms_scale(xd, W.EPS))
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([[0, 255, 256, 8191], np.random.default_rng(7).integers(0, S, 36)]))
+    xr = x[:, toks].astype(np.float64)
+    xs = xr / np.sqrt(np.mean(xr * xr, axis=-1, keepdims=True) + W.EPS)
+    wf = W.bf16_round(w.astype(np.float32) * gi.astype(np.float32))
+    rq, rk, rv = A.qkv_project(xs, *_split(wf, Hq, Hkv), Hq, Hkv)
+    ti = torch.as_tensor(toks, device="cuda")
+    assert_proj(host(q[:, ti]), rq, "q")
+    assert_proj(host(v[:, ti]), rv, "v")
+    ref = A.qknorm_rope(rk[0], gk, W.EPS, toks, base, scale, True).transpose(1, 0, 2)[None]
+    assert_proj(host(kh[:, :, ti]), ref, "khat")
