@@ -49,11 +49,22 @@ constexpr int kTileElems = kBN * 128;  // bf16 elements per tile
 constexpr int kStageStride = 136;      // Q/O staging rows: 256 + 16 B
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-// Per-lane byte offsets of the operand reads inside a tile.
+// LDS: four K tile buffers in the first 64 KiB and four V tile buffers in
+// the next 64 KiB, so every operand read is one per-lane address register
+// plus an immediate offset (buffer, key half or key step) below 64 KiB.
+constexpr int kTileBytes = kTileElems * 2;
+constexpr uint32_t kVRegion = 4 * kTileBytes;
+
+// Per-lane LDS byte addresses of the operand reads in K buffer 0 / V buffer 0.
 struct TileAddr {
   uint32_t k[8];     // K^T operand, dims step st (key half kb adds 32 rows = 8192 B)
   uint32_t v[2][4];  // V^T operand, [row half][dim block] (key step t adds 16 rows = 4096 B)
 };
+
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_at(uint32_t byte_addr) {
+  return (const __attribute__((address_space(3))) T*)(uintptr_t)byte_addr;
+}
 
 __device__ __forceinline__ int wave_min_i(int x) {
 #pragma unroll
@@ -154,10 +165,11 @@ __device__ __forceinline__ void softmax(f32x16 (&s)[2], WaveState& w, bf16x8 (&p
   w.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 }
 
-__device__ __forceinline__ bf16x8 read_v(const uint16_t* vl, const TileAddr& ad, int t, int mb) {
-  const char* base = (const char*)vl + 4096 * t;
-  const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + ad.v[0][mb]));
-  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + ad.v[1][mb]));
+template <int VB>
+__device__ __forceinline__ bf16x8 read_v(const TileAddr& ad, int t, int mb, uint32_t vdyn) {
+  const uint32_t off = VB * kTileBytes + 4096 * t + vdyn;
+  const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lds_at<bf16x4>(ad.v[0][mb] + off));
+  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lds_at<bf16x4>(ad.v[1][mb] + off));
   return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -169,19 +181,20 @@ __device__ __forceinline__ bf16x8 read_v(const uint16_t* vl, const TileAddr& ad,
 // is a hook between the MFMA groups for global->LDS loads; the tile loop
 // passes an empty one (its loads go out at the end of the softmax half, which
 // measured faster than any placement between the MFMAs).
-template <bool DO_PV, bool DO_QK, typename Dma>
-__device__ __forceinline__ void gemm_half(const uint16_t* vl, const uint16_t* kl, const TileAddr& ad,
-                                          const bf16x8 (&pb)[4], const bf16x8 (&q)[8], f32x16 (&s)[2],
-                                          WaveState& w, Dma&& dma) {
+// VB, KB: the V and K buffers (compile-time); vdyn: a run-time byte offset
+// added to the V reads (0 inside the unrolled tile loop).
+template <bool DO_PV, bool DO_QK, int VB, int KB, typename Dma>
+__device__ __forceinline__ void gemm_half(const TileAddr& ad, const bf16x8 (&pb)[4], const bf16x8 (&q)[8],
+                                          f32x16 (&s)[2], WaveState& w, Dma&& dma, uint32_t vdyn = 0) {
   bf16x8 vop[4][4];  // [16-key step][dim block]
   bf16x8 kop[8][2];  // [16-dim step][key half]
   auto rd_v = [&](int t) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) vop[t][mb] = read_v(vl, ad, t, mb);
+    for (int mb = 0; mb < 4; ++mb) vop[t][mb] = read_v<VB>(ad, t, mb, vdyn);
   };
   auto rd_k = [&](int st) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) kop[st][kb] = *(const bf16x8*)((const char*)kl + ad.k[st] + 8192 * kb);
+    for (int kb = 0; kb < 2; ++kb) kop[st][kb] = *lds_at<bf16x8>(ad.k[st] + KB * kTileBytes + 8192 * kb);
   };
   auto mm_pv = [&](int t) {
 #pragma unroll
@@ -256,14 +269,13 @@ __device__ __forceinline__ void gemm_half(const uint16_t* vl, const uint16_t* kl
   }
 }
 
-template <bool DO_PV, typename Dma>
-__device__ __forceinline__ void gemm_step(bool do_qk, const uint16_t* vl, const uint16_t* kl, const TileAddr& ad,
-                                          const bf16x8 (&pb)[4], const bf16x8 (&q)[8], f32x16 (&s)[2],
-                                          WaveState& w, Dma&& dma) {
+template <bool DO_PV, int VB, int KB, typename Dma>
+__device__ __forceinline__ void gemm_step(bool do_qk, const TileAddr& ad, const bf16x8 (&pb)[4],
+                                          const bf16x8 (&q)[8], f32x16 (&s)[2], WaveState& w, Dma&& dma) {
   if (do_qk) {
-    gemm_half<DO_PV, true>(vl, kl, ad, pb, q, s, w, dma);
+    gemm_half<DO_PV, true, VB, KB>(ad, pb, q, s, w, dma);
   } else if (DO_PV) {
-    gemm_half<DO_PV, false>(vl, kl, ad, pb, q, s, w, dma);
+    gemm_half<DO_PV, false, VB, KB>(ad, pb, q, s, w, dma);
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) dma(k);
@@ -295,16 +307,19 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   constexpr int WP = NW * P;   // positions per workgroup
   constexpr int NT = 64 * NW;  // threads per workgroup
   static_assert(NW == 8, "the tile loader gives each wave 8 of the 64 rows");
-  // LDS, 16 KiB per tile buffer: K in 3 buffers and V in 4 (tile t is read,
+  // LDS, 16 KiB per tile buffer: K and V in 4 buffers each (tile t is read,
   // tile t+1 has landed or is landing, tile t+2 is being fetched; V of tile
-  // t-1 is still read by the PV half).  Order: K0 V0 K1 K2 V1 V2 V3.  Each
+  // t-1 is still read by the PV half), tile t in buffer t & 3 so that, with
+  // the loop unrolled by 4, every buffer is a compile-time offset.  Each
   // wave's staging rows for its 32 Q rows (prologue) and O rows (epilogue),
   // through which both move between HBM and registers as whole 256-byte rows,
-  // alias K1..V3: the first tile (K0, V0) lands while Q is staged, and the
-  // second is only fetched once every wave has read its Q rows.
-  static_assert(NW * 32 * kStageStride <= 5 * kTileElems, "staging must fit in K1..V3");
-  auto lds_k = [&](int buf) { return lds + (buf == 0 ? 0 : buf + 1) * kTileElems; };
-  auto lds_v = [&](int buf) { return lds + (buf == 0 ? 1 : buf + 3) * kTileElems; };
+  // alias K1..K3 (waves 0-4) and V1..V3 (waves 5-7): the first tile (K0, V0)
+  // lands while Q is staged, and the second is only fetched once every wave
+  // has read its Q rows.
+  static_assert(5 * 32 * kStageStride <= 3 * kTileElems, "staging of waves 0-4 must fit in K1..K3");
+  static_assert((NW - 5) * 32 * kStageStride <= 3 * kTileElems, "staging of waves 5-7 must fit in V1..V3");
+  auto lds_k = [&](int buf) { return lds + buf * kTileElems; };
+  auto lds_v = [&](int buf) { return lds + (4 + buf) * kTileElems; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -328,7 +343,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
 
   // ---- Q rows of this wave, loaded row-major: 16 lanes x 16 B per row.
   // Staging row x = (head hg, position offset u) is x = hg * P + u.
-  uint16_t* xs = lds + 2 * kTileElems + wave * 32 * kStageStride;
+  uint16_t* xs = wave < 5 ? lds + kTileElems + wave * 32 * kStageStride
+                          : lds + 5 * kTileElems + (wave - 5) * 32 * kStageStride;
   const int x_col = (lane & 15) * 8;
   {
     u32x4 qv[8];
@@ -380,6 +396,16 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   // of the cache (the long-context case) take a straight path: a wave-uniform
   // base plus a per-lane offset, the mode test hoisted out of the per-load
   // code.  Only tiles at the chunk or cache edges check every row.
+  // LDS destination (M0) of this wave's load i (0..1) of a K or V tile
+  // buffer.  The wave's base goes through an opaque copy so that the
+  // compiler forms each destination where it is used instead of holding all
+  // of them in SGPRs across the tile loop.
+  const uint32_t wave_lds_base = lds_addr_of(lds) + (uint32_t)(8 * wave_u * kD * 2);
+  auto dst_of = [&](bool is_v, int buf, int i) {
+    uint32_t wb = wave_lds_base;
+    asm volatile("" : "+s"(wb));
+    return wb + (uint32_t)((is_v ? 4 + buf : buf) * kTileBytes + 4 * i * kD * 2);
+  };
   auto dma_tile = [&](int t, int kbuf, int vbuf) {
     const int ts = p0 + t * kBN;
     const bool in_chunk = t >= 0 && ts + kBN <= chunk_end;
@@ -396,8 +422,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
         const bool is_v = k >= 2;
         const int col = ((lane & 15) ^ ((dma_r << 2) | ((2 * wave + i) & 3))) * 8;
         const int row = 8 * wave + 4 * i + dma_r;
-        const uint16_t* dst = (is_v ? lds_v(vbuf) : lds_k(kbuf)) + (8 * wave_u + 4 * i) * kD;
-        dma16s(is_v ? vb : kb, 2u * (uint32_t)(row * (is_v ? vs : kD) + col), lds_addr_of(dst));
+        dma16s(is_v ? vb : kb, 2u * (uint32_t)(row * (is_v ? vs : kD) + col), dst_of(is_v, is_v ? vbuf : kbuf, i));
       }
       return;
     }
@@ -415,38 +440,20 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
         const long long slot = a.is_ring ? (long long)(j % a.cap) : (long long)j;
         src = (is_v ? cv_bg : ck_bg) + slot * kD;
       }
-      const uint16_t* dst = (is_v ? lds_v(vbuf) : lds_k(kbuf)) + (8 * wave_u + 4 * i) * kD;
-      dma16(src + col, lds_addr_of(dst));
+      dma16(src + col, dst_of(is_v, is_v ? vbuf : kbuf, i));
     }
   };
 
   // Items whose every key tile lies inside the chunk (a self-contained prompt
   // of whole tiles) load each tile from two running bases with per-lane
   // offsets fixed for the item: no per-tile choice of source.
-  // The lane offsets are recomputed per tile from an opaque copy of the lane
-  // index: held across the loop they would not fit next to O, Q and S.
   const bool chunk_only = t_begin >= 0 && p0 + (t_begin + n_t) * kBN <= chunk_end;
-  auto dma_tile_chunk = [&](int t, int kbuf, int vbuf) {
-    const uint16_t* kb = khat_bg + (long long)t * kBN * kD;
-    const uint16_t* vb = v_bg + (long long)t * kBN * vstride;
-    int lo = lane;
-    asm volatile("" : "+v"(lo));
-    const int r = lo >> 4;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = k & 1;
-      const bool is_v = k >= 2;
-      const int col = ((lo & 15) ^ ((r << 2) | ((2 * wave_u + i) & 3))) * 8;
-      const int row = 8 * wave_u + 4 * i + r;
-      const uint16_t* dst = (is_v ? lds_v(vbuf) : lds_k(kbuf)) + (8 * wave_u + 4 * i) * kD;
-      dma16s(is_v ? vb : kb, 2u * (uint32_t)(row * (is_v ? vstride : kD) + col), lds_addr_of(dst));
-    }
-  };
 
   // operand read offsets inside a tile (see TileAddr)
   TileAddr ad;
+  const uint32_t lds0 = lds_addr_of(lds);
 #pragma unroll
-  for (int st = 0; st < 8; ++st) ad.k[st] = ln * 256 + ((((2 * st + h2) ^ swz(ln))) << 4);
+  for (int st = 0; st < 8; ++st) ad.k[st] = lds0 + ln * 256 + ((((2 * st + h2) ^ swz(ln))) << 4);
   {
     const int g4 = lane >> 4, w16 = lane & 15;
 #pragma unroll
@@ -455,7 +462,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
       for (int mb = 0; mb < 4; ++mb) {
         const int row = 8 * hf + 4 * (g4 >> 1) + (w16 >> 2);
         const int c = 4 * mb + 2 * (g4 & 1) + ((w16 & 3) >> 1);
-        ad.v[hf][mb] = row * 256 + ((c ^ swz(row)) << 4) + 8 * (w16 & 1);
+        ad.v[hf][mb] = lds0 + kVRegion + row * 256 + ((c ^ swz(row)) << 4) + 8 * (w16 & 1);
       }
   }
 
@@ -540,6 +547,19 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   // MFMA pipe and the VALU are busy at the same time instead of in turn.
   //   group A (waves 0..NW/2-1): half 1 PV(t-1) + QK(t), half 2 softmax(t)
   //   group B (waves NW/2..NW-1): half 1 softmax(t-1),   half 2 PV(t-1) + QK(t)
+  // Straight chunk tiles: this lane's byte offsets from a tile's first row
+  // for the wave's two 4-row loads (K and V rows share the swizzle), held
+  // for the item, and per-tile bases advanced by one tile per step.
+  uint32_t ck_off[2], cv_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = lane >> 4;
+    const int row = 8 * wave_u + 4 * i + r;
+    const int col = ((lane & 15) ^ ((r << 2) | ((2 * wave_u + i) & 3))) * 8;
+    ck_off[i] = 2u * (uint32_t)(row * kD + col);
+    cv_off[i] = 2u * (uint32_t)(row * vstride + col);
+  }
+
   auto run = [&](auto grp_b_tag, auto chunk_only_tag) {
     constexpr bool GB = decltype(grp_b_tag)::value;
     constexpr bool CHUNK_ONLY = decltype(chunk_only_tag)::value;
@@ -549,11 +569,15 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
     bool have_s = false;  // (group B) s holds scores of the previous tile
     bool s_full = false;
     int s_ts = 0;
-    for (int it = 0; it < n_t; ++it) {
+    // bases of tile t + 2 (straight chunk tiles)
+    const char* kb_next = (const char*)khat_bg + (long long)(t_begin + 2) * (kBN * kD * 2);
+    const char* vb_next = (const char*)v_bg + (long long)(t_begin + 2) * kBN * vstride * 2;
+    // One tile step; tile it sits in K and V buffer U = it & 3.
+    auto step = [&](auto u_tag, int it) {
+      constexpr int U = decltype(u_tag)::value;
+      constexpr int UPREV = (U + 3) & 3;  // V buffer of the previous tile
+      constexpr int UNEXT2 = (U + 2) & 3;
       const int t = t_begin + it;
-      const int kcur = it % 3;
-      const int vcur = it & 3;
-      const int vprev = (it + 3) & 3;
       const int ts = p0 + t * kBN;
       const bool act = ts <= w_hi_max && ts + kBN - 1 >= w_lo_min;
       const bool full = ts >= w_lo_max && ts + kBN - 1 <= w_hi_min;
@@ -563,19 +587,22 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
       const bool fetch = it + 2 < n_t;
       auto prefetch = [&]() {
         if (fetch) {
-          if (CHUNK_ONLY)
-            dma_tile_chunk(t + 2, (it + 2) % 3, (it + 2) & 3);
-          else
-            dma_tile(t + 2, (it + 2) % 3, (it + 2) & 3);
+          if (CHUNK_ONLY) {
+            dma16s(kb_next, ck_off[0], dst_of(false, UNEXT2, 0));
+            dma16s(kb_next, ck_off[1], dst_of(false, UNEXT2, 1));
+            dma16s(vb_next, cv_off[0], dst_of(true, UNEXT2, 0));
+            dma16s(vb_next, cv_off[1], dst_of(true, UNEXT2, 1));
+          } else
+            dma_tile(t + 2, UNEXT2, UNEXT2);
         }
       };
       auto no_dma = [](int) {};
       if (!GB) {
         __builtin_amdgcn_s_setprio(1);
         if (have_p)
-          gemm_step<true>(act, lds_v(vprev), lds_k(kcur), ad, pb, qreg, s, ws, no_dma);
+          gemm_step<true, UPREV, U>(act, ad, pb, qreg, s, ws, no_dma);
         else
-          gemm_step<false>(act, lds_v(vprev), lds_k(kcur), ad, pb, qreg, s, ws, no_dma);
+          gemm_step<false, UPREV, U>(act, ad, pb, qreg, s, ws, no_dma);
         __builtin_amdgcn_s_setprio(0);
         have_p = false;
         barrier_lds();
@@ -595,9 +622,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
         barrier_lds();
         __builtin_amdgcn_s_setprio(1);
         if (have_p)
-          gemm_step<true>(act, lds_v(vprev), lds_k(kcur), ad, pb, qreg, s, ws, no_dma);
+          gemm_step<true, UPREV, U>(act, ad, pb, qreg, s, ws, no_dma);
         else
-          gemm_step<false>(act, lds_v(vprev), lds_k(kcur), ad, pb, qreg, s, ws, no_dma);
+          gemm_step<false, UPREV, U>(act, ad, pb, qreg, s, ws, no_dma);
         __builtin_amdgcn_s_setprio(0);
         have_p = false;
         have_s = act;
@@ -606,15 +633,32 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
         wait_tile_loads_but(fetch ? 4 : 0);
         barrier_lds();
       }
+      if (CHUNK_ONLY) {
+        kb_next += kBN * kD * 2;
+        vb_next += (long long)kBN * vstride * 2;
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    for (int it = 0; it < n_t; it += 4) {
+      step(I0{}, it);
+      if (it + 1 >= n_t) break;
+      step(I1{}, it + 1);
+      if (it + 2 >= n_t) break;
+      step(I2{}, it + 2);
+      if (it + 3 >= n_t) break;
+      step(I3{}, it + 3);
     }
-    const int vprev = (n_t + 3) & 3;  // V buffer of the last tile
     // drain: the last tile's PV (group A) / softmax then PV (group B)
     if (GB && have_s) {
       softmax_tile<ONLINE>(s_full, s, ws, pb, row_lo, row_hi, s_ts, h2);
       have_p = true;
     }
     barrier_lds();
-    if (have_p) gemm_half<true, false>(lds_v(vprev), lds_k(0), ad, pb, qreg, s, ws, [](int) {});
+    if (have_p)  // V of the last tile sits in buffer (n_t - 1) & 3
+      gemm_half<true, false, 0, 0>(ad, pb, qreg, s, ws, [](int) {}, (uint32_t)(((n_t - 1) & 3) * kTileBytes));
   };
   if (wave_u >= NW / 2) {
     if (chunk_only)
@@ -684,7 +728,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
 template <int G, bool ONLINE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW)
 void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[7 * kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[8 * kTileElems];
   const int n_items = a.B * a.Hkv * a.n_qtiles;
   const int li0 = (!ONLINE && (int)gridDim.x == n_items)
                       ? prefill_item_of_workgroup(blockIdx.x, n_items, prefill_rank_major(a.local, a.B * a.Hkv))
