@@ -173,11 +173,11 @@ __device__ __forceinline__ bf16x8 read_v(const TileAddr& ad, int t, int mb, uint
   return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// The matrix half of a tile step: PV of the previous tile (if DO_PV) then QK
-// of this one (if DO_QK), 16 + 16 MFMAs.  LDS operand reads run two PV steps
-// (256 MFMA cycles) or four QK steps ahead of the MFMAs that use them, and
-// scheduling fences keep the compiler from pulling them back next to their
-// uses, where each MFMA would wait out a full LDS latency.  dma(k), k = 0..7,
+// The matrix half of a tile step: QK of this tile (if DO_QK) then PV of the
+// previous one (if DO_PV), 16 + 16 MFMAs.  LDS operand reads run four QK
+// steps or two PV steps (256 MFMA cycles) ahead of the MFMAs that use them,
+// and scheduling fences keep the compiler from pulling them back next to
+// their uses, where each MFMA would wait out a full LDS latency.  dma(k), k = 0..7,
 // is a hook between the MFMA groups for global->LDS loads; the tile loop
 // passes an empty one (its loads go out at the end of the softmax half, which
 // measured faster than any placement between the MFMAs).
@@ -212,60 +212,42 @@ __device__ __forceinline__ void gemm_half(const TileAddr& ad, const bf16x8 (&pb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
   }
-  constexpr int KA = DO_PV ? 6 : 4;  // K steps read before the first QK MFMA
-  if (DO_PV) {
-    rd_v(0);
-    rd_v(1);
-  }
+  // QK first: its K operands (ds_read_b128) arrive sooner than the
+  // transposed V reads, which get the whole QK run as lead time.
+  constexpr int KA = 4;  // K steps read ahead of their QK MFMAs (6 measured slower)
   if (DO_QK) {
-    rd_k(0);
-    rd_k(1);
-  }
-  fence();
-  if (DO_PV) {
-    mm_pv(0);
-    rd_v(2);
-    dma(0);
+#pragma unroll
+    for (int st = 0; st < KA; ++st) rd_k(st);
     fence();
-    mm_pv(1);
-    rd_v(3);
-    dma(1);
-    fence();
-    mm_pv(2);
-    if (DO_QK) {
-      rd_k(2);
-      rd_k(3);
-    }
-    dma(2);
-    fence();
-    mm_pv(3);
-    if (DO_QK) {
-      rd_k(4);
-      rd_k(5);
-    }
-    dma(3);
-    fence();
-  } else if (DO_QK) {
-    rd_k(2);
-    rd_k(3);
-    fence();
-  }
-  if (DO_QK) {
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       mm_qk(st);
       if (st + KA < 8) rd_k(st + KA);
-      if (DO_PV) {
-        if (st & 1) dma(4 + (st >> 1));
-      } else {
-        dma(st);
-      }
+      if (DO_PV && st >= 4 && st < 6) rd_v(st - 4);
+      dma(st);
       fence();
     }
   }
-  if (DO_PV && !DO_QK) {
+  if (DO_PV) {
+    if (!DO_QK) {
+      rd_v(0);
+      rd_v(1);
+      fence();
+    }
+    mm_pv(0);
+    rd_v(2);
+    fence();
+    mm_pv(1);
+    rd_v(3);
+    fence();
+    mm_pv(2);
+    fence();
+    mm_pv(3);
+    fence();
+  }
+  if (!DO_QK) {
 #pragma unroll
-    for (int k = 4; k < 8; ++k) dma(k);
+    for (int k = 0; k < 8; ++k) dma(k);
   }
 }
 
