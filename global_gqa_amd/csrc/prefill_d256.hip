@@ -312,9 +312,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
     return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
-  // Matrix half: PV of the tile in slot vs (o[mb] += V^T P^T, 16 MFMAs),
-  // then, if DO_QK, S^T of the tile in slot ks (16 MFMAs).  Operands are
-  // read two MFMAs ahead through a 3-register rotation.
+  // Matrix half: if DO_QK, S^T of the tile in slot ks (16 MFMAs), then PV of
+  // the tile in slot vs (o[mb] += V^T P^T, 16 MFMAs).  Operands are read two
+  // MFMAs ahead through a 3-register rotation.
   auto mfma_half = [&](auto do_qk_tag, int vs, int ks, const bf16x8 (&pb)[2], f32x16& s) {
     constexpr bool DO_QK = decltype(do_qk_tag)::value;
     constexpr int NM = DO_QK ? 32 : 16;
@@ -323,17 +323,26 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
     const uint32_t vb = vbase + vs * kSlotBytes;
     const uint32_t kb = kbase + ks * kSlotBytes;
     bf16x8 op[kAhead + 1];
-    auto rd = [&](int k) __attribute__((always_inline)) { return k < 16 ? rd_v(vb, k) : rd_k(kb, k - 16); };
+    // step k of the half: the 16 QK steps first (when DO_QK), then the 16 PV
+    // steps (the transposed V reads get the QK run as lead time)
+    auto is_pv = [&](int k) { return !DO_QK || k >= 16; };
+    auto pv_idx = [&](int k) { return DO_QK ? k - 16 : k; };
+    auto qk_idx = [&](int k) { return k; };
+    auto rd = [&](int k) __attribute__((always_inline)) {
+      return is_pv(k) ? rd_v(vb, pv_idx(k)) : rd_k(kb, qk_idx(k));
+    };
 #pragma unroll
     for (int k = 0; k < kAhead; ++k) op[k] = rd(k);
     fence256();
 #pragma unroll
     for (int k = 0; k < NM; ++k) {
-      if (k < 16)
-        o[k & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[k % (kAhead + 1)], pb[k >> 3], o[k & 7], 0, 0, 0);
-      else
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[k % (kAhead + 1)], qreg[k - 16], k == 16 ? f32x16{} : s, 0,
-                                                    0, 0);
+      if (is_pv(k)) {
+        const int j = pv_idx(k);
+        o[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[k % (kAhead + 1)], pb[j >> 3], o[j & 7], 0, 0, 0);
+      } else {
+        const int j = qk_idx(k);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[k % (kAhead + 1)], qreg[j], j == 0 ? f32x16{} : s, 0, 0, 0);
+      }
       if (k + kAhead < NM) op[(k + kAhead) % (kAhead + 1)] = rd(k + kAhead);
       fence256();
     }
