@@ -116,6 +116,21 @@ __host__ __device__ inline void prefill_item_coords(int li, int n_groups, int nq
 // the run-major blocks for their L2 reuse.
 __host__ __device__ inline bool prefill_rank_major(bool local, int n_groups) { return !local && n_groups % 8 != 0; }
 
+// Local layers with K = items / workgroups > 1 (nq a multiple of K):
+// workgroup slot s (an XCD's slots are consecutive) takes the K query tiles
+// j, j + nq/K, ..., j + (K-1) nq/K of one (sequence, kv head) run, the last
+// (latest rank: the lightest, near the start of the sequence) first.  The
+// workgroups that hold one of a run's short first tiles then run out of step
+// with the rest, so the item boundaries, where every workgroup loads its Q
+// rows and first K/V tiles at once, are spread over time.  At each step an
+// XCD's workgroups cover nq/K consecutive query tiles of each of its runs.
+__host__ __device__ inline int prefill_spread_item(int s, int kk, int K, int nq) {
+  const int per = nq / K;
+  const int bg = s / per, j = s - bg * per;
+  const int k = kk == 0 ? K - 1 : kk - 1;
+  return bg * nq + j + per * k;
+}
+
 // Logical item of hardware workgroup x in a launch of n = n_groups * nq
 // workgroups, one item each.
 __host__ __device__ inline int prefill_item_of_workgroup(int x, int n, bool rank_major) {

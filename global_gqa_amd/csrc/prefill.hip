@@ -700,12 +700,16 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   }
 }
 
-// Workgroup g takes items xcd_remap(g) + k * gridDim.x: with fewer
-// workgroups than items (the local layers, whose items all cost the same)
-// each workgroup runs several items back to back on its CU, and the
-// workgroups of one XCD always work on neighbouring query tiles of the same
-// kv head, which share K/V in that XCD's L2.  With one workgroup per item
-// (the fast pass of a global layer) the item order is that of
+// With fewer workgroups than items (the local layers, whose items cost
+// about the same) each workgroup runs several items back to back on its CU:
+// the query tiles prefill_spread_item gives it (one run, tiles nq/K apart,
+// the lightest first, so that the workgroups holding a run's short first
+// tiles fall out of step and item boundaries, where every workgroup loads
+// its Q rows and first tiles at once, spread out: local layers 169 -> 159 us
+// at the 27B shape), and the workgroups of one XCD work on neighbouring
+// query tiles of the same kv head, which share K/V in that XCD's L2.  Other
+// counts take items xcd_remap(g) + k * gridDim.x.  With one workgroup per
+// item (the fast pass of a global layer) the item order is that of
 // prefill_item_of_workgroup.
 template <int G, bool ONLINE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW)
@@ -723,6 +727,12 @@ void prefill_fwd(PrefillArgs a, Pos0Table p0t, SpanTable spt, RopeTable rt) {
     for (int li = li0 + (int)(threadIdx.x & 63) * (int)gridDim.x; li < n_items; li += 64 * (int)gridDim.x)
       any |= a.flags[li];
     if (__builtin_amdgcn_ballot_w64(any != 0) == 0) return;
+  }
+  const int per_wg = n_items / (int)gridDim.x;
+  if (!ONLINE && a.local && per_wg > 1 && n_items % (int)gridDim.x == 0 && a.n_qtiles % per_wg == 0) {
+    for (int kk = 0; kk < per_wg; ++kk)
+      prefill_item<G, ONLINE, NW>(a, p0t, spt, rt, lds, prefill_spread_item(li0, kk, per_wg, a.n_qtiles));
+    return;
   }
   for (int li = li0; li < n_items; li += gridDim.x) prefill_item<G, ONLINE, NW>(a, p0t, spt, rt, lds, li);
 }

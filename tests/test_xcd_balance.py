@@ -80,3 +80,29 @@ def test_local_layers_keep_runs_together(exe):
     for xcd in range(8):
         qts = sorted(qt for x, _, _, qt in it if x == xcd)
         assert qts == list(range(qts[0], qts[0] + 64)), xcd
+
+
+@pytest.mark.parametrize("n_groups,nq,grid", [(16, 64, 256), (16, 32, 256), (2, 32, 32), (1, 512, 256)])
+def test_local_spread_schedule(exe, n_groups, nq, grid):
+    """Local layers with several items per workgroup: every item runs exactly
+    once; every workgroup whose items include one of a run's short first
+    query tiles (qt < 8: fewer keys than the window) runs it first, so those
+    workgroups fall out of step with the rest; at every step an XCD's
+    workgroups cover consecutive query tiles of at most a few runs (their K/V
+    windows overlap in that XCD's L2)."""
+    out = subprocess.run([exe, str(n_groups), str(nq), "1", str(grid)], capture_output=True, text=True, check=True)
+    it = np.array([[int(t) for t in line.split()] for line in out.stdout.split("\n") if line.strip()])
+    n, K = n_groups * nq, n_groups * nq // grid
+    assert sorted(it[:, 2].tolist()) == list(range(n))
+    per_wg = it.reshape(grid, K, 5)
+    for w in per_wg:
+        qts = w[:, 4].tolist()
+        assert len(set(w[:, 3].tolist())) == 1  # one run per workgroup
+        if min(qts) < 8:
+            assert qts[0] == min(qts)
+    for xcd in range(8):
+        for kk in range(K):
+            sel = it[(it[:, 0] == xcd) & (it[:, 1] == kk)]
+            for bg in set(sel[:, 3].tolist()):
+                q = sorted(sel[sel[:, 3] == bg][:, 4].tolist())
+                assert q == list(range(q[0], q[0] + len(q))), (xcd, kk, bg, q)
