@@ -104,7 +104,7 @@ __device__ __forceinline__ uint32_t lds_addr_of(const uint16_t* p) {
 
 // Per-wave running state of the flash loop (one query row per lane).
 struct WaveState {
-  f32x16 o[4];   // O^T accumulators [dim block of 32] (stay in AGPRs)
+  f32x16 o[4];   // O^T accumulators [dim block of 32]
   float l;       // per-lane partial row sum of p
   float m;       // running max (log2 units), online-maximum pass only
 };
@@ -183,9 +183,10 @@ __device__ __forceinline__ bf16x8 read_v(const TileAddr& ad, int t, int mb, uint
 // measured faster than any placement between the MFMAs).
 // VB, KB: the V and K buffers (compile-time); vdyn: a run-time byte offset
 // added to the V reads (0 inside the unrolled tile loop).
-template <bool DO_PV, bool DO_QK, int VB, int KB, typename Dma>
+template <bool DO_PV, bool DO_QK, int VB, int KB, bool PRE = false, typename Dma>
 __device__ __forceinline__ void gemm_half(const TileAddr& ad, const bf16x8 (&pb)[4], const bf16x8 (&q)[8],
-                                          f32x16 (&s)[2], WaveState& w, Dma&& dma, uint32_t vdyn = 0) {
+                                          f32x16 (&s)[2], WaveState& w, Dma&& dma, uint32_t vdyn = 0,
+                                          const bf16x8 (&pre)[4] = {}) {
   bf16x8 vop[4][4];  // [16-key step][dim block]
   bf16x8 kop[8][2];  // [16-dim step][key half]
   auto rd_v = [&](int t) {
@@ -201,23 +202,27 @@ __device__ __forceinline__ void gemm_half(const TileAddr& ad, const bf16x8 (&pb)
     for (int mb = 0; mb < 4; ++mb)
       w.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][mb], pb[t], w.o[mb], 0, 0, 0);
   };
-  auto mm_qk = [&](int st) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[st][kb], q[st], s[kb], 0, 0, 0);
-  };
-  auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
-  if (DO_QK) {
+  auto mm_qk = [&](int st) {  // step 0 starts the sums from zero
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-  }
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[st][kb], q[st], st == 0 ? f32x16{} : s[kb], 0, 0, 0);
+  };
+  auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
   // QK first: its K operands (ds_read_b128) arrive sooner than the
   // transposed V reads, which get the whole QK run as lead time.
   constexpr int KA = 4;  // K steps read ahead of their QK MFMAs (6 measured slower)
   if (DO_QK) {
+    if (PRE) {  // K of steps 0 and 1 read before the barrier that opens the half
+      kop[0][0] = pre[0];
+      kop[0][1] = pre[1];
+      kop[1][0] = pre[2];
+      kop[1][1] = pre[3];
 #pragma unroll
-    for (int st = 0; st < KA; ++st) rd_k(st);
+      for (int st = 2; st < KA; ++st) rd_k(st);
+    } else {
+#pragma unroll
+      for (int st = 0; st < KA; ++st) rd_k(st);
+    }
     fence();
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
@@ -251,11 +256,12 @@ __device__ __forceinline__ void gemm_half(const TileAddr& ad, const bf16x8 (&pb)
   }
 }
 
-template <bool DO_PV, int VB, int KB, typename Dma>
+template <bool DO_PV, int VB, int KB, bool PRE, typename Dma>
 __device__ __forceinline__ void gemm_step(bool do_qk, const TileAddr& ad, const bf16x8 (&pb)[4],
-                                          const bf16x8 (&q)[8], f32x16 (&s)[2], WaveState& w, Dma&& dma) {
+                                          const bf16x8 (&q)[8], f32x16 (&s)[2], WaveState& w, Dma&& dma,
+                                          const bf16x8 (&pre)[4]) {
   if (do_qk) {
-    gemm_half<DO_PV, true, VB, KB>(ad, pb, q, s, w, dma);
+    gemm_half<DO_PV, true, VB, KB, PRE>(ad, pb, q, s, w, dma, 0, pre);
   } else if (DO_PV) {
     gemm_half<DO_PV, false, VB, KB>(ad, pb, q, s, w, dma);
   } else {
@@ -582,9 +588,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
       if (!GB) {
         __builtin_amdgcn_s_setprio(1);
         if (have_p)
-          gemm_step<true, UPREV, U>(act, ad, pb, qreg, s, ws, no_dma);
+          gemm_step<true, UPREV, U, false>(act, ad, pb, qreg, s, ws, no_dma, {});
         else
-          gemm_step<false, UPREV, U>(act, ad, pb, qreg, s, ws, no_dma);
+          gemm_step<false, UPREV, U, false>(act, ad, pb, qreg, s, ws, no_dma, {});
         __builtin_amdgcn_s_setprio(0);
         have_p = false;
         barrier_lds();
@@ -601,12 +607,23 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
           have_p = true;
         }
         prefetch();
+        // Group B reads K of its first two QK steps while it waits at the
+        // barrier that opens its matrix half (the tile was published by the
+        // previous step's closing barrier), so its MFMAs start without an
+        // LDS round trip after the barrier.  (Group A's matrix half opens a
+        // step; holding V^T operands across the step boundary for it, with
+        // its steps rotated to keep them local, measured slower.)
+        bf16x8 kpre[4];
+        if (act) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kpre[i] = *lds_at<bf16x8>(ad.k[i >> 1] + U * kTileBytes + 8192 * (i & 1));
+        }
         barrier_lds();
         __builtin_amdgcn_s_setprio(1);
         if (have_p)
-          gemm_step<true, UPREV, U>(act, ad, pb, qreg, s, ws, no_dma);
+          gemm_step<true, UPREV, U, true>(act, ad, pb, qreg, s, ws, no_dma, kpre);
         else
-          gemm_step<false, UPREV, U>(act, ad, pb, qreg, s, ws, no_dma);
+          gemm_step<false, UPREV, U, true>(act, ad, pb, qreg, s, ws, no_dma, kpre);
         __builtin_amdgcn_s_setprio(0);
         have_p = false;
         have_s = act;
