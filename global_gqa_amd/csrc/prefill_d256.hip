@@ -315,8 +315,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   // Matrix half: if DO_QK, S^T of the tile in slot ks (16 MFMAs), then PV of
   // the tile in slot vs (o[mb] += V^T P^T, 16 MFMAs).  Operands are read two
   // MFMAs ahead through a 3-register rotation.
-  auto mfma_half = [&](auto do_qk_tag, int vs, int ks, const bf16x8 (&pb)[2], f32x16& s) {
+  // pre: with PRE, the K operands of the first kAhead QK steps, already read
+  auto mfma_half = [&](auto do_qk_tag, auto pre_tag, int vs, int ks, const bf16x8 (&pb)[2], f32x16& s,
+                       const bf16x8 (&pre)[kAhead]) {
     constexpr bool DO_QK = decltype(do_qk_tag)::value;
+    constexpr bool PRE = decltype(pre_tag)::value && DO_QK;
     constexpr int NM = DO_QK ? 32 : 16;
     uint32_t kbase, vbase;
     operand_bases(kbase, vbase);
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
       return is_pv(k) ? rd_v(vb, pv_idx(k)) : rd_k(kb, qk_idx(k));
     };
 #pragma unroll
-    for (int k = 0; k < kAhead; ++k) op[k] = rd(k);
+    for (int k = 0; k < kAhead; ++k) op[k] = PRE ? pre[k] : rd(k);
     fence256();
 #pragma unroll
     for (int k = 0; k < NM; ++k) {
@@ -406,6 +409,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
   // PV(-1) runs with P = 0 on the zeroed V region of slot 3.
   auto run = [&](auto grp_b_tag) __attribute__((always_inline)) {
     constexpr bool GB = decltype(grp_b_tag)::value;
+    const bf16x8 no_pre[kAhead] = {};
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = NEG_INF;
@@ -422,7 +426,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
       const int ks = it & (kNB - 1);
       if (!GB) {
         __builtin_amdgcn_s_setprio(1);
-        mfma_half(std::true_type{}, vs, ks, pb, s);
+        mfma_half(std::true_type{}, std::false_type{}, vs, ks, pb, s, no_pre);
         __builtin_amdgcn_s_setprio(0);
         barrier_lds();
         softmax(s, ts, full, pb);
@@ -430,9 +434,18 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
       } else {
         softmax(s, s_ts, s_full, pb);
         if (fetch) dma_tile(t + 2, (it + 2) & (kNB - 1));
+        // the first QK operands read while waiting at the barrier (the tile
+        // was published by the previous step's closing barrier)
+        bf16x8 kpre[kAhead];
+        {
+          uint32_t kb0, vb0;
+          operand_bases(kb0, vb0);
+#pragma unroll
+          for (int k = 0; k < kAhead; ++k) kpre[k] = rd_k(kb0 + ks * kSlotBytes, k);
+        }
         barrier_lds();
         __builtin_amdgcn_s_setprio(1);
-        mfma_half(std::true_type{}, vs, ks, pb, s);
+        mfma_half(std::true_type{}, std::true_type{}, vs, ks, pb, s, kpre);
         __builtin_amdgcn_s_setprio(0);
         s_ts = ts;
         s_full = full;
@@ -446,7 +459,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_fwd_d256(PrefillArgs a, P
     // drain: PV of the last tile (group B first runs its softmax)
     if (GB) softmax(s, s_ts, s_full, pb);
     barrier_lds();
-    mfma_half(std::false_type{}, (n_t + kNB - 1) & (kNB - 1), 0, pb, s);
+    mfma_half(std::false_type{}, std::false_type{}, (n_t + kNB - 1) & (kNB - 1), 0, pb, s, no_pre);
   };
   if (wave_u >= kNW / 2)
     run(std::true_type{});
