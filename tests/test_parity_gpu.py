@@ -270,6 +270,40 @@ def test_decode_against_cache(kind, is_ring, cap, Hq, Hkv):
     assert_rowwise_bf16(host(cache.k), rck, "cache k after decode append")
 
 
+# Split shapes where the halving of short-cache splits lands on one workgroup
+# per CU: the 1B model's 32 sequences on 1024-slot rings (256 splits of 128
+# slots, as in its decode step), a short global cache over 8 sequences (256
+# splits of 256 slots), and head dimension 128 with 16 sequences of a
+# 4096-slot cache (256 splits of 256 slots).
+@pytest.mark.parametrize("D,B,Hq,Hkv,kind,is_ring,cap", [(256, 32, 4, 1, A.LOCAL, True, 1024),
+                                                         (256, 8, 4, 1, A.GLOBAL, False, 8192),
+                                                         (128, 16, 8, 1, A.GLOBAL, False, 4096)])
+def test_decode_one_workgroup_per_cu_grid(D, B, Hq, Hkv, kind, is_ring, cap):
+    seed = 9100 + D + B
+    rng = np.random.default_rng(seed)
+    hi = 3 * cap if is_ring else cap
+    positions = rng.integers(0, hi, size=B).astype(np.int32)
+    positions[:3] = [0, cap - 1, hi - 1]
+    if is_ring:
+        positions[3] = cap  # the first wrap of the ring
+    base, scale = _kind_params(kind, 8.0)
+    ck = W.host_normal_bf16((B, Hkv, cap, D), seed)
+    cv = W.host_normal_bf16((B, Hkv, cap, D), seed + 1)
+    q = W.host_normal_bf16((B, Hq, D), seed + 2)
+    kn = W.host_normal_bf16((B, Hkv, D), seed + 3)
+    vn = W.host_normal_bf16((B, Hkv, D), seed + 4)
+    gq, gk = W.host_gamma(D, seed + 5), W.host_gamma(D, seed + 6)
+    cache = G.KVCache(dev_bf16(ck), dev_bf16(cv), is_ring)
+    maxp = int(positions.max())
+    o = G.decode(dev_bf16(q), dev_bf16(kn), dev_bf16(vn), torch.from_numpy(positions).cuda(), maxp, cache, kind,
+                 W.WINDOW, base, scale, dev_f32(gq), dev_f32(gk), W.EPS)
+    torch.cuda.synchronize()
+    ref, rck, rcv = A.decode(q, kn, vn, ck, cv, is_ring, positions, kind, W.WINDOW, base, scale, gq, gk, W.EPS)
+    assert_parity(host(o), ref, f"decode one workgroup per CU D={D} B={B} kind={kind}")
+    assert np.array_equal(host(cache.v), rcv)
+    assert_rowwise_bf16(host(cache.k), rck, "cache k after decode append")
+
+
 # A cache slot never written (a fresh allocation past a sequence's end) may hold
 # NaN.  Rows the token cannot see get probability 0, and 0 * NaN must not reach
 # the sums: the kernels drop such rows' values, not only their weights.
