@@ -550,8 +550,9 @@ __global__ __launch_bounds__(1024) void decode_combine(DecodeArgs a) {
   // The thread's splits are read kCombineBatch at a time, all loads issued
   // before the first is used (one memory round trip per batch instead of
   // one per split: a 32K cache's 64 splits at D = 256 are 16 per thread),
-  // then folded in the same order as one at a time.
-  constexpr int kCombineBatch = 16;
+  // then folded in the same order as one at a time.  Eight keep the kernel
+  // within 64 VGPRs, two 1024-thread workgroups per CU.
+  constexpr int kCombineBatch = 8;
   for (int c0 = grp; c0 < a.n_chunks; c0 += kCombineGroups * kCombineBatch) {
     float mv[kCombineBatch], xv[kCombineBatch], lv[kCombineBatch];
 #pragma unroll
