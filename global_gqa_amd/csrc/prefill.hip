@@ -436,6 +436,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
   // of whole tiles) load each tile from two running bases with per-lane
   // offsets fixed for the item: no per-tile choice of source.
   const bool chunk_only = t_begin >= 0 && p0 + (t_begin + n_t) * kBN <= chunk_end;
+  // Items over a linear cache (the long-context chunk against its cache)
+  // whose tiles are whole cache tiles below the chunk, then whole chunk
+  // tiles: the same two running bases, switched once where the chunk starts.
+  const bool linear_run = !chunk_only && a.has_cache && !a.is_ring && p0 + t_begin * kBN >= kmin_avail &&
+                          p0 + (t_begin + n_t) * kBN <= chunk_end;
 
   // operand read offsets inside a tile (see TileAddr)
   TileAddr ad;
@@ -548,9 +553,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
     cv_off[i] = 2u * (uint32_t)(row * vstride + col);
   }
 
-  auto run = [&](auto grp_b_tag, auto chunk_only_tag) {
+  // mode: 0 any tile (per-tile choice of source), 1 chunk tiles only, 2 linear-cache tiles then chunk tiles
+  auto run = [&](auto grp_b_tag, auto mode_tag) {
     constexpr bool GB = decltype(grp_b_tag)::value;
-    constexpr bool CHUNK_ONLY = decltype(chunk_only_tag)::value;
+    constexpr int MODE = decltype(mode_tag)::value;
+    constexpr bool CHUNK_ONLY = MODE == 1;
+    constexpr bool LINEAR_RUN = MODE == 2;
     f32x16 s[2];
     bf16x8 pb[4];
     bool have_p = false;  // pb holds p of the previous tile, PV still to do
@@ -560,6 +568,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
     // bases of tile t + 2 (straight chunk tiles)
     const char* kb_next = (const char*)khat_bg + (long long)(t_begin + 2) * (kBN * kD * 2);
     const char* vb_next = (const char*)v_bg + (long long)(t_begin + 2) * kBN * vstride * 2;
+    if (LINEAR_RUN && t_begin + 2 < 0) {  // cache tiles: slot = position, rows of kD elements for K and V
+      kb_next = (const char*)ck_bg + (long long)(p0 + (t_begin + 2) * kBN) * (kD * 2);
+      vb_next = (const char*)cv_bg + (long long)(p0 + (t_begin + 2) * kBN) * (kD * 2);
+    }
     // One tile step; tile it sits in K and V buffer U = it & 3.
     auto step = [&](auto u_tag, int it) {
       constexpr int U = decltype(u_tag)::value;
@@ -580,6 +592,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
             dma16s(kb_next, ck_off[1], dst_of(false, UNEXT2, 1));
             dma16s(vb_next, cv_off[0], dst_of(true, UNEXT2, 0));
             dma16s(vb_next, cv_off[1], dst_of(true, UNEXT2, 1));
+          } else if (LINEAR_RUN) {
+            const bool from_cache = t + 2 < 0;  // cache V rows are kD apart, the chunk's vstride
+            const uint32_t v0 = from_cache ? ck_off[0] : cv_off[0];
+            const uint32_t v1 = from_cache ? ck_off[1] : cv_off[1];
+            dma16s(kb_next, ck_off[0], dst_of(false, UNEXT2, 0));
+            dma16s(kb_next, ck_off[1], dst_of(false, UNEXT2, 1));
+            dma16s(vb_next, v0, dst_of(true, UNEXT2, 0));
+            dma16s(vb_next, v1, dst_of(true, UNEXT2, 1));
           } else
             dma_tile(t + 2, UNEXT2, UNEXT2);
         }
@@ -636,6 +656,15 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
         kb_next += kBN * kD * 2;
         vb_next += (long long)kBN * vstride * 2;
       }
+      if (LINEAR_RUN) {  // bases of the next step's tile t + 3
+        if (t + 3 == 0) {
+          kb_next = (const char*)khat_bg;
+          vb_next = (const char*)v_bg;
+        } else {
+          kb_next += kBN * kD * 2;
+          vb_next += t + 3 < 0 ? (long long)kBN * kD * 2 : (long long)kBN * vstride * 2;
+        }
+      }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -659,16 +688,23 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const Pos0Tab
     if (have_p)  // V of the last tile sits in buffer (n_t - 1) & 3
       gemm_half<true, false, 0, 0>(ad, pb, qreg, s, ws, [](int) {}, (uint32_t)(((n_t - 1) & 3) * kTileBytes));
   };
+  using M0 = std::integral_constant<int, 0>;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
   if (wave_u >= NW / 2) {
     if (chunk_only)
-      run(std::true_type{}, std::true_type{});
+      run(std::true_type{}, M1{});
+    else if (linear_run)
+      run(std::true_type{}, M2{});
     else
-      run(std::true_type{}, std::false_type{});
+      run(std::true_type{}, M0{});
   } else {
     if (chunk_only)
-      run(std::false_type{}, std::true_type{});
+      run(std::false_type{}, M1{});
+    else if (linear_run)
+      run(std::false_type{}, M2{});
     else
-      run(std::false_type{}, std::false_type{});
+      run(std::false_type{}, M0{});
   }
 
   // Fast pass (ONLINE = false): QK-RMSNorm bounds every logit by
